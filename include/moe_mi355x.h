@@ -1,0 +1,198 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X (gfx950) forward pass of one sparse
+ * Mixture-of-Experts FFN layer with the Step-3.5-Flash layer shape.
+ *
+ * What the layer computes (sources: the Step-3.5-Flash pages):
+ *   - hyper.ai summary of arXiv 2602.10604, section "方法" (Method): each token
+ *     goes to 8 of 288 routed experts plus one always-on shared expert.
+ *   - shd-paper.top summary, "方法详解 / 关键设计": a gating network maps the
+ *     token representation to one weight per expert; the highest-weighted
+ *     experts are used.
+ *   - paperlayer.ai summary, App. B (Detail Analysis of Localized Activation
+ *     Blow-up): SwiGLU experts (gate and up activations multiplied
+ *     element-wise); the residual stream is normalised with RMSNorm.
+ *   - LLM Atlas model card "Step-3.5-Flash", raw config field table:
+ *     hidden_size 4096, moe_num_experts 288, moe_top_k 8,
+ *     moe_intermediate_size 1280, share_expert_dim 1280, need_fp32_gate,
+ *     moe_router_activation sigmoid, use_moe_router_bias,
+ *     norm_expert_weight, moe_router_scaling_factor 3, swiglu_limits,
+ *     zero_centered, torch_dtype bfloat16.
+ *
+ *   logits l[t,e] = sum_h float(x[t,h]) * W_r[e,h]          (fp32)
+ *   score  s[t,e] = 1 / (1 + exp(-l[t,e]))
+ *   key    k[t,e] = s[t,e] + b[e]          (bias steers selection only)
+ *   sel[t]        = the K largest keys, equal keys -> lower expert index,
+ *                   listed in ascending expert id
+ *   w[t,j]        = scale * s[t,sel_j] / sum_j' s[t,sel_j']   (norm_topk=1)
+ *   FFN_e(v)      = Wd_e (silu(Wg_e v) * (Wu_e v)),  silu(z) = z/(1+e^-z)
+ *   y[t]          = sum_j w[t,j] FFN_{sel_j}(x[t]) + FFN_shared(x[t])
+ *
+ * Conventions for every entry point:
+ *   - Pointers named in the structs and arguments are DEVICE pointers unless
+ *     marked "host".  The caller owns every buffer; the library allocates and
+ *     frees nothing.  Scratch memory comes from the caller's workspace.
+ *   - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ *   - Arrays are dense row-major; every device pointer must be 16-byte
+ *     aligned.  Weights are read-only; x and y must not alias.
+ *   - Calls are asynchronous on `stream` and never synchronise.  Argument
+ *     checks run on the host before any HIP call, in the fixed order
+ *     null -> shape -> option -> alignment -> workspace; a failed check
+ *     returns a negative moe_status and sets moe_last_error().  A failed
+ *     kernel launch returns MOE_ERR_DEVICE.  Faults during execution show
+ *     up at the caller's next synchronisation of the stream.
+ *   - The same inputs give bitwise-identical outputs (no float atomics).
+ *   - Calls that share a workspace must not overlap in time.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL                   */
+  MOE_ERR_SHAPE = -2,       /* a size is out of the supported range         */
+  MOE_ERR_OPTION = -3,      /* an option value is invalid                   */
+  MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_workspace_bytes() */
+  MOE_ERR_ALIGN = -5,       /* a device pointer is not 16-byte aligned      */
+  MOE_ERR_DEVICE = -6       /* a HIP call or kernel launch failed           */
+} moe_status;
+
+/* Layer sizes (host struct).
+ *   T  tokens, 1 <= T <= 1<<20
+ *   H  hidden size, a multiple of 128, 128 <= H <= 16384     (Flash: 4096)
+ *   E  routed experts, 1 <= E <= 1024                          (Flash: 288)
+ *   K  experts per token, 1 <= K <= min(E, 16)                 (Flash: 8)
+ *   I  routed intermediate size, a multiple of 64, <= 16384    (Flash: 1280)
+ *   Is shared intermediate size, 0 (no shared expert) or a multiple of 64
+ *                                                              (Flash: 1280) */
+typedef struct { int32_t T, H, E, K, I, Is; } moe_dims;
+
+/* Routing and activation options (host struct).
+ *   route_scale      moe_router_scaling_factor (Flash: 3.0); finite, > 0
+ *   norm_topk        norm_expert_weight: 1 = normalise the K selected scores
+ *                    to sum 1 before scaling (Flash), 0 = w = scale * s
+ *   bias_in_weights  0 = the bias steers selection only (default reading);
+ *                    1 = the weights also use s + b
+ *   swiglu_limit     0 = off.  > 0: the routed experts clamp the gate
+ *                    pre-activation from above at +limit and the up
+ *                    projection to [-limit, +limit] before the product
+ *                    (model card: swiglu_limits, 0 for most layers)
+ *   swiglu_limit_shared  the same for the shared expert */
+typedef struct {
+  float route_scale;
+  int32_t norm_topk;
+  int32_t bias_in_weights;
+  float swiglu_limit;
+  float swiglu_limit_shared;
+} moe_opts;
+
+/* Router: W [E,H] fp32, b [E] fp32 (learned bias, may be all zero). */
+typedef struct { const float* W; const float* b; } moe_router;
+
+/* Routed experts, bf16: w_gate [E,I,H], w_up [E,I,H], w_down [E,H,I]. */
+typedef struct { const uint16_t* w_gate; const uint16_t* w_up; const uint16_t* w_down; } moe_experts;
+
+/* Shared expert, bf16: w_gate [Is,H], w_up [Is,H], w_down [H,Is].
+ * Pass NULL (or set dims.Is = 0) for a layer without a shared expert. */
+typedef struct { const uint16_t* w_gate; const uint16_t* w_up; const uint16_t* w_down; } moe_shared;
+
+/* Routing outputs (device buffers owned by the caller).
+ *   topk_idx   [T,K] int32  selected experts, ascending per token
+ *   topk_w     [T,K] fp32   combine weights
+ *   counts     [E]   int32  slots routed to each expert (sum = T*K)
+ *   offsets    [E+1] int32  exclusive prefix sum of counts, offsets[E] = T*K
+ *   perm_token [T*K] int32  token of each expert-contiguous row; inside an
+ *                           expert's block rows are in ascending token order
+ *   slot_pos   [T,K] int32  the row that holds token t's slot j
+ *   keys       [T,E] fp32   optional (may be NULL): selection keys s + b
+ *   scores     [T,E] fp32   optional (may be NULL): sigmoid scores s     */
+typedef struct {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm_token;
+  int32_t* slot_pos;
+  float* keys;
+  float* scores;
+} moe_routing;
+
+/* Byte offsets of the intermediates inside a workspace (host struct), for
+ * inspection by tests.  h is bf16 [(T*K)*I + T*Is]: routed rows of width I
+ * in expert-contiguous order, then the shared expert's T rows of width Is.
+ * o is bf16 [T*K + T, H]: each row already multiplied by its combine weight
+ * (shared rows by 1). */
+typedef struct { size_t h, o, total; } moe_ws_layout;
+
+/* ABI version of the library (MOE_ABI_VERSION of the header it was built
+ * from). */
+int32_t moe_abi_version(void);
+
+/* Message of the last failed call on this thread (host string owned by the
+ * library; valid until the next call on this thread; "" after success). */
+const char* moe_last_error(void);
+
+/* Workspace bytes that moe_route and moe_forward need for `d` (host).
+ * Returns 0 if `d` is NULL or out of range. */
+size_t moe_workspace_bytes(const moe_dims* d);
+
+/* Offsets of h and o in a workspace for `d`.  Returns MOE_ERR_NULL or
+ * MOE_ERR_SHAPE on bad arguments. */
+moe_status moe_workspace_layout(const moe_dims* d, moe_ws_layout* out);
+
+/* Steps 1-4 of the layer: router logits, sigmoid, biased top-K, weights and
+ * the expert-contiguous dispatch (counts, offsets, perm_token, slot_pos).
+ *   d, opts  host structs; opts may be NULL (Flash defaults: scale 3,
+ *            normalised, bias for selection only, no clamp)
+ *   x        [T,H] bf16 token representations
+ *   router   host struct holding device pointers W and b
+ *   out      host struct; all members except keys/scores must be non-NULL
+ *   ws       device workspace of ws_bytes >= moe_workspace_bytes(d) */
+moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                     const moe_router* router, const moe_routing* out,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* The whole layer: moe_route, then per expert the gated FFN on its rows
+ * (bf16 MFMA, fp32 accumulation, h rounded to bf16), the shared expert on
+ * every token, and the weighted combine back to token order (fp32 sum in
+ * slot order, shared last, rounded once to bf16).
+ *   experts      host struct of device pointers (all non-NULL)
+ *   shared       host struct or NULL; must be non-NULL with non-NULL
+ *                members iff d->Is > 0
+ *   y            [T,H] bf16 output
+ *   routing_out  NULL, or a moe_routing as for moe_route to receive the
+ *                routing (then the workspace keeps no copy of it)
+ *   ws           device workspace of ws_bytes >= moe_workspace_bytes(d) */
+moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                       const moe_router* router, const moe_experts* experts,
+                       const moe_shared* shared, uint16_t* y,
+                       const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Glue between chained layers of a pre-norm residual stream (paperlayer.ai
+ * summary, App. B: RMSNorm over the summed layer outputs; model card:
+ * zero_centered).  For each of the T rows of width H:
+ *   r      = r_in + y_add            (fp32 add, stored to r_out as bf16;
+ *                                     y_add may be NULL: r = r_in)
+ *   x_out  = bf16( r' / sqrt(mean(r'^2) + eps) * (1 + gamma) )
+ * where r' is the bf16 value stored for r.  gamma [H] fp32 may be NULL
+ * (gain 1).  r_out may be NULL when y_add is NULL; x_out may be NULL (no
+ * norm).  r_out may alias r_in.  H must be a multiple of 128; eps >= 0. */
+moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
+                                const uint16_t* y_add, const float* gamma, float eps,
+                                uint16_t* r_out, uint16_t* x_out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

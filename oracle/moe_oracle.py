@@ -37,6 +37,8 @@ constant below):
   A6  SwiGLU: h = silu(Wg x) * (Wu x), silu(z) = z / (1 + exp(-z)).
   A7  the shared expert is added with weight 1 (not scaled by 3).
   A8  no SwiGLU clamp on the hot path (a limit of 0 means "off").
+  A17 a positive SwiGLU limit clamps the gate from above and the up
+      projection to [-limit, limit].
   A12 if the selected scores sum to 0, weights are uniform scale/K.
   A13 no capacity limit, no token dropping.  A14 no group-limited routing.
   A15 RMSNorm epsilon 1e-6, zero-centred gain (1 + gamma).
@@ -163,15 +165,24 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(xr, Wg, Wu, Wd, return_hidden: bool = False):
+def swiglu_ffn(xr, Wg, Wu, Wd, return_hidden: bool = False, limit: float = 0.0):
     """One gated expert on rows xr [m, H]: h = silu(xr Wg^T) * (xr Wu^T),
     o = h Wd^T.  Wg, Wu are [I, H]; Wd is [H, I].  [P3 App.B]: SwiGLU, the
     product of the gate and up activations; the three matrices of size
     4096 x 1280 per expert are what the 196B/11B parameter counts of
-    [P3 2.2] add up to.  No clamp (reading A8)."""
+    [P3 2.2] add up to.
+
+    `limit` is [P4 config] swiglu_limits: 0 = no clamp (reading A8, the
+    value of almost every layer).  A positive limit clamps the gate
+    pre-activation from above and the up projection to [-limit, limit]
+    before the product (reading A17; the pages name the limit, not its
+    form)."""
     xr = _f64(xr)
     g = xr @ _f64(Wg).T
     u = xr @ _f64(Wu).T
+    if limit > 0:
+        g = np.minimum(g, limit)
+        u = np.clip(u, -limit, limit)
     h = silu(g) * u
     o = h @ _f64(Wd).T
     return (o, h) if return_hidden else o
@@ -192,7 +203,8 @@ def route(x, Wr, b, K: int, scale: float = 3.0, norm: bool = True,
 
 def moe_layer(x, Wr, b, Wg, Wu, Wd, Ws_g=None, Ws_u=None, Ws_d=None, K: int = 8,
               scale: float = 3.0, norm: bool = True, bias_in_weights: bool = False,
-              sel: Optional[np.ndarray] = None, return_parts: bool = False):
+              sel: Optional[np.ndarray] = None, return_parts: bool = False,
+              limit: float = 0.0, limit_shared: float = 0.0):
     """y_t = sum_j w[t,j] * FFN_{sel_j}(x_t) + S(x_t), computed expert by
     expert over the dispatch of `route`.  [P1 Method], [P3 2.2]: 8 of 288
     routed experts plus one always-on shared expert; the shared expert adds
@@ -213,11 +225,11 @@ def moe_layer(x, Wr, b, Wg, Wu, Wd, Ws_g=None, Ws_u=None, Ws_d=None, K: int = 8,
     routed = np.zeros_like(x)
     for e in np.unique(sel):
         rows_t, rows_j = np.nonzero(sel == e)
-        o = swiglu_ffn(x[rows_t], Wg[e], Wu[e], Wd[e])
+        o = swiglu_ffn(x[rows_t], Wg[e], Wu[e], Wd[e], limit=limit)
         routed[rows_t] += w[rows_t, rows_j][:, None] * o
     shared = np.zeros_like(x)
     if Ws_g is not None:
-        shared = swiglu_ffn(x, Ws_g, Ws_u, Ws_d)
+        shared = swiglu_ffn(x, Ws_g, Ws_u, Ws_d, limit=limit_shared)
     y = routed + shared
     if return_parts:
         r.update(y=y, routed=routed, shared=shared)

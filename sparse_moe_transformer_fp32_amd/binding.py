@@ -1,0 +1,288 @@
+"""Thin ctypes binding of the gfx950 C-ABI library `libsmoe_gfx950.so`.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch provides device memory and the stream (`tensor.data_ptr()`
+and `torch.cuda.current_stream().cuda_stream`).  There is no fallback: if
+the library is missing, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsmoe_gfx950.so")
+ABI_VERSION = 1
+
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_OPTION = 0, -1, -2, -3
+MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_DEVICE = -4, -5, -6
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_OPTION",
+                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_DEVICE"}
+
+EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
+            "moe_route", "moe_forward", "moe_residual_rmsnorm"]
+
+_vp = ctypes.c_void_p
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H", "E", "K", "I", "Is")]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("route_scale", ctypes.c_float), ("norm_topk", ctypes.c_int32),
+                ("bias_in_weights", ctypes.c_int32), ("swiglu_limit", ctypes.c_float),
+                ("swiglu_limit_shared", ctypes.c_float)]
+
+
+class Router(ctypes.Structure):
+    _fields_ = [("W", _vp), ("b", _vp)]
+
+
+class Experts(ctypes.Structure):
+    _fields_ = [("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
+
+
+class Shared(ctypes.Structure):
+    _fields_ = [("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
+
+
+class Routing(ctypes.Structure):
+    _fields_ = [(n, _vp) for n in ("topk_idx", "topk_w", "counts", "offsets", "perm_token",
+                                   "slot_pos", "keys", "scores")]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_size_t), ("o", ctypes.c_size_t), ("total", ctypes.c_size_t)]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library {LIB_PATH} is not built; run "
+                           "`python -m sparse_moe_transformer_fp32_amd.build` first")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.moe_abi_version.restype = ctypes.c_int32
+    lib.moe_abi_version.argtypes = []
+    lib.moe_last_error.restype = ctypes.c_char_p
+    lib.moe_last_error.argtypes = []
+    lib.moe_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_workspace_bytes.argtypes = [P(Dims)]
+    lib.moe_workspace_layout.restype = ctypes.c_int
+    lib.moe_workspace_layout.argtypes = [P(Dims), P(WsLayout)]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_route.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Routing), _vp, ctypes.c_size_t, _vp]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Experts), P(Shared), _vp,
+                                P(Routing), _vp, ctypes.c_size_t, _vp]
+    lib.moe_residual_rmsnorm.restype = ctypes.c_int
+    lib.moe_residual_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
+                                         ctypes.c_float, _vp, _vp, _vp]
+    v = lib.moe_abi_version()
+    if v != ABI_VERSION:
+        raise RuntimeError(f"{LIB_PATH}: ABI version {v}, binding expects {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().moe_last_error().decode()
+
+
+def _check(status: int):
+    if status != MOE_OK:
+        raise MoEError(status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def make_opts(route_scale=3.0, norm_topk=True, bias_in_weights=False, swiglu_limit=0.0,
+              swiglu_limit_shared=0.0) -> Opts:
+    return Opts(float(route_scale), int(bool(norm_topk)), int(bool(bias_in_weights)),
+                float(swiglu_limit), float(swiglu_limit_shared))
+
+
+def dims(T, H, E, K, I, Is) -> Dims:
+    return Dims(int(T), int(H), int(E), int(K), int(I), int(Is))
+
+
+def workspace_bytes(T, H, E, K, I, Is) -> int:
+    d = dims(T, H, E, K, I, Is)
+    n = load().moe_workspace_bytes(ctypes.byref(d))
+    if n == 0:
+        raise MoEError(MOE_ERR_SHAPE, last_error())
+    return n
+
+
+def workspace_layout(T, H, E, K, I, Is) -> WsLayout:
+    d = dims(T, H, E, K, I, Is)
+    out = WsLayout()
+    _check(load().moe_workspace_layout(ctypes.byref(d), ctypes.byref(out)))
+    return out
+
+
+def alloc_workspace(T, H, E, K, I, Is, device="cuda") -> torch.Tensor:
+    return torch.empty(workspace_bytes(T, H, E, K, I, Is), dtype=torch.uint8, device=device)
+
+
+def alloc_routing(T, E, K, device="cuda", keys=False) -> Dict[str, torch.Tensor]:
+    i32, f32 = torch.int32, torch.float32
+    r = dict(topk_idx=torch.empty((T, K), dtype=i32, device=device),
+             topk_w=torch.empty((T, K), dtype=f32, device=device),
+             counts=torch.empty(E, dtype=i32, device=device),
+             offsets=torch.empty(E + 1, dtype=i32, device=device),
+             perm_token=torch.empty(T * K, dtype=i32, device=device),
+             slot_pos=torch.empty((T, K), dtype=i32, device=device))
+    if keys:
+        r["keys"] = torch.empty((T, E), dtype=f32, device=device)
+        r["scores"] = torch.empty((T, E), dtype=f32, device=device)
+    return r
+
+
+def _routing_struct(r: Dict[str, torch.Tensor]) -> Routing:
+    return Routing(*[_ptr(r.get(n)) for n in ("topk_idx", "topk_w", "counts", "offsets",
+                                               "perm_token", "slot_pos", "keys", "scores")])
+
+
+def route(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor, K: int, *,
+          I: int = 64, Is: int = 0, keys: bool = False, ws: Optional[torch.Tensor] = None,
+          out: Optional[Dict[str, torch.Tensor]] = None, **opts) -> Dict[str, torch.Tensor]:
+    """Router and dispatch (moe_route).  I/Is only size the workspace."""
+    lib = load()
+    _dev(x, "x", torch.bfloat16)
+    _dev(router_w, "router_w", torch.float32)
+    _dev(router_b, "router_b", torch.float32)
+    T, H = x.shape
+    E = router_w.shape[0]
+    d = dims(T, H, E, K, I, Is)
+    if ws is None:
+        ws = alloc_workspace(T, H, E, K, I, Is, x.device)
+    r = out if out is not None else alloc_routing(T, E, K, x.device, keys)
+    o = make_opts(**opts)
+    rt = Router(_ptr(router_w), _ptr(router_b))
+    rs = _routing_struct(r)
+    _check(lib.moe_route(ctypes.byref(d), ctypes.byref(o), _ptr(x), ctypes.byref(rt),
+                         ctypes.byref(rs), _ptr(ws), ws.numel(), _stream(x.device)))
+    return r
+
+
+class MoELayer:
+    """One MoE FFN layer bound to device weights, with its workspace and
+    output buffer allocated once (calls allocate nothing)."""
+
+    def __init__(self, router_w, router_b, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
+                 ws_down=None, K=8, T_max=None, **opts):
+        load()
+        _dev(router_w, "router_w", torch.float32)
+        _dev(router_b, "router_b", torch.float32)
+        for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+            _dev(t, n, torch.bfloat16)
+        self.E, self.H = router_w.shape
+        self.I = w_gate.shape[1]
+        self.K = int(K)
+        self.Is = 0 if ws_gate is None else ws_gate.shape[0]
+        if self.Is:
+            for n, t in (("ws_gate", ws_gate), ("ws_up", ws_up), ("ws_down", ws_down)):
+                _dev(t, n, torch.bfloat16)
+        self.tensors = (router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
+        self.router = Router(_ptr(router_w), _ptr(router_b))
+        self.experts = Experts(_ptr(w_gate), _ptr(w_up), _ptr(w_down))
+        self.shared = Shared(_ptr(ws_gate), _ptr(ws_up), _ptr(ws_down)) if self.Is else None
+        self.opts = make_opts(**opts)
+        self.device = router_w.device
+        self._ws = None
+        if T_max:
+            self.reserve(T_max)
+
+    def reserve(self, T: int) -> int:
+        need = workspace_bytes(T, self.H, self.E, self.K, self.I, self.Is)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return need
+
+    def workspace(self) -> torch.Tensor:
+        return self._ws
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                routing: Optional[Dict[str, torch.Tensor]] = None) -> torch.Tensor:
+        lib = load()
+        _dev(x, "x", torch.bfloat16)
+        T = x.shape[0]
+        if x.shape[1] != self.H:
+            raise ValueError(f"x has {x.shape[1]} columns, layer hidden size is {self.H}")
+        ws_bytes = self.reserve(T)
+        if y is None:
+            y = torch.empty_like(x)
+        _dev(y, "y", torch.bfloat16)
+        d = dims(T, self.H, self.E, self.K, self.I, self.Is)
+        rs = _routing_struct(routing) if routing is not None else None
+        _check(lib.moe_forward(ctypes.byref(d), ctypes.byref(self.opts), _ptr(x),
+                               ctypes.byref(self.router), ctypes.byref(self.experts),
+                               ctypes.byref(self.shared) if self.shared is not None else None,
+                               _ptr(y), ctypes.byref(rs) if rs is not None else None,
+                               _ptr(self._ws), ws_bytes, _stream(x.device)))
+        return y
+
+    __call__ = forward
+
+
+def forward(x, router_w, router_b, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,
+            K=8, routing: bool = False, keys: bool = False, **opts):
+    """One call of moe_forward with freshly allocated buffers.  With
+    routing=True also returns the routing tensors."""
+    layer = MoELayer(router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down, K=K, **opts)
+    r = alloc_routing(x.shape[0], layer.E, K, x.device, keys) if routing else None
+    y = layer.forward(x, routing=r)
+    return (y, r, layer) if routing else y
+
+
+def residual_rmsnorm(r_in: torch.Tensor, y_add: Optional[torch.Tensor] = None,
+                     gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                     r_out: Optional[torch.Tensor] = None, x_out: Optional[torch.Tensor] = None,
+                     want_r: bool = True, want_x: bool = True):
+    """r = r_in + y_add (bf16), x = RMSNorm(r) (bf16), via moe_residual_rmsnorm."""
+    lib = load()
+    _dev(r_in, "r_in", torch.bfloat16)
+    T, H = r_in.shape
+    if y_add is not None:
+        _dev(y_add, "y_add", torch.bfloat16)
+        if r_out is None and want_r:
+            r_out = torch.empty_like(r_in)
+    if gamma is not None:
+        _dev(gamma, "gamma", torch.float32)
+    if x_out is None and want_x:
+        x_out = torch.empty_like(r_in)
+    _check(lib.moe_residual_rmsnorm(T, H, _ptr(r_in), _ptr(y_add), _ptr(gamma), float(eps),
+                                    _ptr(r_out), _ptr(x_out), _stream(r_in.device)))
+    return r_out, x_out

@@ -1,0 +1,342 @@
+// C-ABI entry points: argument checks (host only, before any HIP call), the
+// tiling plan, workspace carving and the kernel launch sequence.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <algorithm>
+#include <string>
+
+#include "moe_mi355x.h"
+#include "smoe_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_err.clear();
+  return MOE_OK;
+}
+
+size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+moe_status check_shape(const moe_dims* d) {
+  if (d->T < 1 || d->T > (1 << 20))
+    return fail(MOE_ERR_SHAPE, "T=%d out of range [1, 1048576]", d->T);
+  if (d->H < 128 || d->H > 16384 || d->H % 128)
+    return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", d->H);
+  if (d->E < 1 || d->E > 1024) return fail(MOE_ERR_SHAPE, "E=%d out of range [1, 1024]", d->E);
+  if (d->K < 1 || d->K > 16 || d->K > d->E)
+    return fail(MOE_ERR_SHAPE, "K=%d must be in [1, min(E=%d, 16)]", d->K, d->E);
+  if (d->I < 64 || d->I > 16384 || d->I % 64)
+    return fail(MOE_ERR_SHAPE, "I=%d must be a multiple of 64 in [64, 16384]", d->I);
+  if (d->Is < 0 || d->Is > 16384 || d->Is % 64)
+    return fail(MOE_ERR_SHAPE, "Is=%d must be 0 or a multiple of 64 up to 16384", d->Is);
+  return MOE_OK;
+}
+
+moe_status check_opts(const moe_opts* o) {
+  if (!o) return MOE_OK;
+  if (!isfinite(o->route_scale) || o->route_scale <= 0.f)
+    return fail(MOE_ERR_OPTION, "route_scale must be finite and > 0");
+  if (o->norm_topk != 0 && o->norm_topk != 1) return fail(MOE_ERR_OPTION, "norm_topk must be 0 or 1");
+  if (o->bias_in_weights != 0 && o->bias_in_weights != 1)
+    return fail(MOE_ERR_OPTION, "bias_in_weights must be 0 or 1");
+  if (!isfinite(o->swiglu_limit) || o->swiglu_limit < 0.f ||
+      !isfinite(o->swiglu_limit_shared) || o->swiglu_limit_shared < 0.f)
+    return fail(MOE_ERR_OPTION, "swiglu limits must be finite and >= 0");
+  return MOE_OK;
+}
+
+moe_opts default_opts() {
+  moe_opts o;
+  o.route_scale = 3.0f;
+  o.norm_topk = 1;
+  o.bias_in_weights = 0;
+  o.swiglu_limit = 0.f;
+  o.swiglu_limit_shared = 0.f;
+  return o;
+}
+
+moe_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MOE_OK;
+}
+
+struct RouteBufs {
+  int32_t *topk_idx, *counts, *offsets, *perm, *slot;
+  float *topk_w, *keys, *scores;
+};
+
+moe_status run_route(const smoe::Plan& p, const moe_opts& o, const uint16_t* x,
+                     const moe_router* router, const RouteBufs& rbuf, char* ws, hipStream_t s) {
+  float* partial = reinterpret_cast<float*>(ws + p.ws_partial);
+  moe_status st;
+  if ((st = launched(smoe::launch_route_logits(p, x, router->W, partial, s), "route_logits")))
+    return st;
+  if ((st = launched(smoe::launch_route_topk(p, partial, router->b, o.route_scale, o.norm_topk,
+                                             o.bias_in_weights, rbuf.topk_idx, rbuf.topk_w,
+                                             rbuf.keys, rbuf.scores, s),
+                     "route_topk")))
+    return st;
+  return launched(
+      smoe::launch_dispatch(p, rbuf.topk_idx, rbuf.topk_w, rbuf.counts, rbuf.offsets, rbuf.perm,
+                            rbuf.slot, reinterpret_cast<int32_t*>(ws + p.ws_row_token),
+                            reinterpret_cast<float*>(ws + p.ws_row_w),
+                            reinterpret_cast<smoe::RowBlock*>(ws + p.ws_rb),
+                            reinterpret_cast<int32_t*>(ws + p.ws_nrb), s),
+      "dispatch");
+}
+
+RouteBufs bufs_from(const moe_routing* r) {
+  return RouteBufs{r->topk_idx, r->counts, r->offsets, r->perm_token, r->slot_pos,
+                   r->topk_w,   r->keys,   r->scores};
+}
+
+RouteBufs bufs_from_ws(const smoe::Plan& p, char* ws) {
+  return RouteBufs{reinterpret_cast<int32_t*>(ws + p.ws_topk_idx),
+                   reinterpret_cast<int32_t*>(ws + p.ws_counts),
+                   reinterpret_cast<int32_t*>(ws + p.ws_offsets),
+                   reinterpret_cast<int32_t*>(ws + p.ws_perm),
+                   reinterpret_cast<int32_t*>(ws + p.ws_slot),
+                   reinterpret_cast<float*>(ws + p.ws_topk_w),
+                   nullptr,
+                   nullptr};
+}
+
+moe_status check_routing_out(const moe_routing* r, bool for_route) {
+  if (!r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm_token || !r->slot_pos)
+    return fail(MOE_ERR_NULL, "%s: routing output members must be non-NULL (keys/scores optional)",
+                for_route ? "moe_route" : "moe_forward");
+  return MOE_OK;
+}
+
+moe_status check_routing_align(const moe_routing* r) {
+  const void* ptrs[] = {r->topk_idx, r->topk_w, r->counts, r->offsets,
+                        r->perm_token, r->slot_pos, r->keys, r->scores};
+  for (const void* q : ptrs)
+    if (q && misaligned(q)) return fail(MOE_ERR_ALIGN, "routing output pointer %p not 16-byte aligned", q);
+  return MOE_OK;
+}
+
+}  // namespace
+
+namespace smoe {
+
+void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
+  *p = Plan{};
+  p->T = T; p->H = H; p->E = E; p->K = K; p->I = I; p->Is = Is;
+  p->KT = T * K;
+  p->rows_total = p->KT + (Is > 0 ? T : 0);
+
+  // router: 16-token tiles for decode, 64 otherwise; split H until the
+  // launch has ~256 workgroups (each split keeps >= 128 columns)
+  p->route_tok = T <= 16 ? 16 : 64;
+  const int tiles = ((T + p->route_tok - 1) / p->route_tok) * ((E + 63) / 64);
+  int S = 1;
+  while (S < 32 && tiles * S < 256 && H % (2 * S * 128) == 0) S *= 2;
+  p->route_splits = S;
+
+  // grouped GEMMs: row-block height follows the mean rows per expert
+  const double avg = (double)K * T / E;
+  int nb = avg <= 16 ? 1 : avg <= 32 ? 2 : avg <= 64 ? 4 : 8;
+  if (nb == 8 && !(I % 128 == 0 && Is % 128 == 0 && H % 256 == 0)) nb = 4;
+  p->nb = nb;
+  p->bn = 16 * nb;
+  p->rb_max = std::min(E, p->KT) + p->KT / p->bn + (Is > 0 ? (T + p->bn - 1) / p->bn : 0);
+  if (nb == 1) {
+    p->ksplit_gu = 4;
+    p->ksplit_dn = (I % 128 == 0 && Is % 128 == 0) ? 4 : 2;
+    p->gu_rows_wg = 64 / p->ksplit_gu;
+    p->dn_rows_wg = 128 / p->ksplit_dn;
+  } else if (nb < 8) {
+    p->ksplit_gu = p->ksplit_dn = 1;
+    p->gu_rows_wg = 64;
+    p->dn_rows_wg = 128;
+  } else {
+    p->ksplit_gu = p->ksplit_dn = 1;
+    p->gu_rows_wg = 128;
+    p->dn_rows_wg = 256;
+  }
+  p->gu_tiles = std::max(I, Is) / p->gu_rows_wg;
+  p->dn_tiles = H / p->dn_rows_wg;
+
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t KT = (size_t)p->KT;
+  p->ws_partial = take((size_t)S * T * E * 4);
+  p->ws_topk_idx = take(KT * 4);
+  p->ws_topk_w = take(KT * 4);
+  p->ws_counts = take((size_t)E * 4);
+  p->ws_offsets = take((size_t)(E + 1) * 4);
+  p->ws_perm = take(KT * 4);
+  p->ws_slot = take(KT * 4);
+  p->ws_row_token = take((size_t)p->rows_total * 4);
+  p->ws_row_w = take((size_t)p->rows_total * 4);
+  p->ws_rb = take((size_t)p->rb_max * sizeof(RowBlock));
+  p->ws_nrb = take(16);
+  p->ws_h = take((KT * I + (size_t)T * Is) * 2);
+  p->ws_o = take((size_t)p->rows_total * H * 2);
+  p->ws_total = off;
+}
+
+}  // namespace smoe
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_last_error(void) { return g_err.c_str(); }
+
+size_t moe_workspace_bytes(const moe_dims* d) {
+  if (!d) {
+    fail(MOE_ERR_NULL, "moe_workspace_bytes: dims is NULL");
+    return 0;
+  }
+  if (check_shape(d) != MOE_OK) return 0;
+  smoe::Plan p;
+  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
+  ok();
+  return p.ws_total;
+}
+
+moe_status moe_workspace_layout(const moe_dims* d, moe_ws_layout* out) {
+  if (!d || !out) return fail(MOE_ERR_NULL, "moe_workspace_layout: NULL argument");
+  moe_status st = check_shape(d);
+  if (st) return st;
+  smoe::Plan p;
+  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
+  out->h = p.ws_h;
+  out->o = p.ws_o;
+  out->total = p.ws_total;
+  return ok();
+}
+
+moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                     const moe_router* router, const moe_routing* out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (!d || !x || !router || !router->W || !router->b || !out || !ws)
+    return fail(MOE_ERR_NULL, "moe_route: NULL argument (dims, x, router, router->W/b, out, ws)");
+  moe_status st = check_routing_out(out, true);
+  if (st) return st;
+  if ((st = check_shape(d))) return st;
+  if ((st = check_opts(opts))) return st;
+  if (misaligned(x) || misaligned(router->W) || misaligned(router->b) || misaligned(ws))
+    return fail(MOE_ERR_ALIGN, "moe_route: x, router W/b and ws must be 16-byte aligned");
+  if ((st = check_routing_align(out))) return st;
+  smoe::Plan p;
+  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
+  if (ws_bytes < p.ws_total)
+    return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes < required %zu", ws_bytes,
+                p.ws_total);
+  const moe_opts o = opts ? *opts : default_opts();
+  if ((st = run_route(p, o, x, router, bufs_from(out), static_cast<char*>(ws), stream))) return st;
+  return ok();
+}
+
+moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                       const moe_router* router, const moe_experts* experts,
+                       const moe_shared* shared, uint16_t* y, const moe_routing* routing_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!d || !x || !router || !router->W || !router->b || !experts || !experts->w_gate ||
+      !experts->w_up || !experts->w_down || !y || !ws)
+    return fail(MOE_ERR_NULL,
+                "moe_forward: NULL argument (dims, x, router, router->W/b, experts->w_*, y, ws)");
+  moe_status st;
+  if (d->Is > 0 && (!shared || !shared->w_gate || !shared->w_up || !shared->w_down))
+    return fail(MOE_ERR_NULL, "moe_forward: Is=%d but the shared expert weights are NULL", d->Is);
+  if (routing_out && (st = check_routing_out(routing_out, false))) return st;
+  if ((st = check_shape(d))) return st;
+  if ((st = check_opts(opts))) return st;
+  if (misaligned(x) || misaligned(router->W) || misaligned(router->b) ||
+      misaligned(experts->w_gate) || misaligned(experts->w_up) || misaligned(experts->w_down) ||
+      misaligned(y) || misaligned(ws))
+    return fail(MOE_ERR_ALIGN, "moe_forward: device pointers must be 16-byte aligned");
+  if (d->Is > 0 && (misaligned(shared->w_gate) || misaligned(shared->w_up) ||
+                    misaligned(shared->w_down)))
+    return fail(MOE_ERR_ALIGN, "moe_forward: shared expert pointers must be 16-byte aligned");
+  if (routing_out && (st = check_routing_align(routing_out))) return st;
+  if (x == y) return fail(MOE_ERR_OPTION, "moe_forward: x and y must not alias");
+  smoe::Plan p;
+  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
+  if (ws_bytes < p.ws_total)
+    return fail(MOE_ERR_WORKSPACE, "moe_forward: workspace %zu bytes < required %zu", ws_bytes,
+                p.ws_total);
+  const moe_opts o = opts ? *opts : default_opts();
+  char* w = static_cast<char*>(ws);
+  const RouteBufs rb = routing_out ? bufs_from(routing_out) : bufs_from_ws(p, w);
+  if ((st = run_route(p, o, x, router, rb, w, stream))) return st;
+
+  const smoe::RowBlock* rbl = reinterpret_cast<const smoe::RowBlock*>(w + p.ws_rb);
+  const int32_t* nrb = reinterpret_cast<const int32_t*>(w + p.ws_nrb);
+  uint16_t* h = reinterpret_cast<uint16_t*>(w + p.ws_h);
+  uint16_t* ob = reinterpret_cast<uint16_t*>(w + p.ws_o);
+  const bool has_sh = d->Is > 0;
+
+  smoe::GateUpArgs ga{};
+  ga.wg = experts->w_gate;
+  ga.wu = experts->w_up;
+  ga.sg = has_sh ? shared->w_gate : nullptr;
+  ga.su = has_sh ? shared->w_up : nullptr;
+  ga.x = x;
+  ga.row_token = reinterpret_cast<const int32_t*>(w + p.ws_row_token);
+  ga.rb = rbl;
+  ga.n_rb = nrb;
+  ga.h = h;
+  ga.limit = o.swiglu_limit;
+  ga.limit_shared = o.swiglu_limit_shared;
+  if ((st = launched(smoe::launch_gate_up(p, ga, stream), "gate_up"))) return st;
+
+  smoe::DownArgs da{};
+  da.wd = experts->w_down;
+  da.sd = has_sh ? shared->w_down : nullptr;
+  da.h = h;
+  da.row_w = reinterpret_cast<const float*>(w + p.ws_row_w);
+  da.rb = rbl;
+  da.n_rb = nrb;
+  da.o = ob;
+  if ((st = launched(smoe::launch_down(p, da, stream), "down"))) return st;
+
+  if ((st = launched(smoe::launch_combine(p, ob, rb.slot, y, stream), "combine"))) return st;
+  return ok();
+}
+
+moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
+                                const uint16_t* y_add, const float* gamma, float eps,
+                                uint16_t* r_out, uint16_t* x_out, hipStream_t stream) {
+  if (!r_in) return fail(MOE_ERR_NULL, "moe_residual_rmsnorm: r_in is NULL");
+  if (y_add && !r_out && !x_out)
+    return fail(MOE_ERR_NULL, "moe_residual_rmsnorm: y_add given but both r_out and x_out NULL");
+  if (!y_add && !x_out) return fail(MOE_ERR_NULL, "moe_residual_rmsnorm: nothing to compute");
+  if (T < 1 || T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T=%d out of range [1, 1048576]", T);
+  if (H < 128 || H > 16384 || H % 128)
+    return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", H);
+  if (!isfinite(eps) || eps < 0.f) return fail(MOE_ERR_OPTION, "eps must be finite and >= 0");
+  if (misaligned(r_in) || misaligned(y_add) || misaligned(gamma) || misaligned(r_out) ||
+      misaligned(x_out))
+    return fail(MOE_ERR_ALIGN, "moe_residual_rmsnorm: pointers must be 16-byte aligned");
+  moe_status st = launched(
+      smoe::launch_residual_rmsnorm(T, H, r_in, y_add, gamma, eps, r_out, x_out, stream),
+      "residual_rmsnorm");
+  if (st) return st;
+  return ok();
+}
+
+}  // extern "C"

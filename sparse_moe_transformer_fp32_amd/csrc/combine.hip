@@ -1,0 +1,138 @@
+// Combine (un-permute) and the residual + RMSNorm glue between chained layers.
+//
+// Sources: shd-paper.top summary, 方法详解 / 关键设计 (the selected experts'
+// outputs are mixed with the gate weights); hyper.ai summary, 方法 (one
+// always-on shared expert per MoE layer); paperlayer.ai summary, App. B
+// (RMSNorm over the summed layer outputs); LLM Atlas model card
+// "Step-3.5-Flash", raw config field table: zero_centered.
+#include "smoe_internal.h"
+
+namespace smoe {
+
+__device__ inline void bf16x8_to_f32(const u32x4& v, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+__device__ inline uint32_t pack2(float a, float b) {
+  const __bf16 ha = (__bf16)a, hb = (__bf16)b;
+  return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+}
+
+// y[t] = sum_j o[slot_pos[t,j]] + o[KT + t]: rows already carry their
+// weights.  fp32 sum in slot order, shared expert last, one rounding.  No
+// atomics: each thread owns 8 columns of one token.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ o,
+                                                      const int32_t* __restrict__ slot_pos,
+                                                      uint16_t* __restrict__ y, int T, int H,
+                                                      int K, int KT, int has_shared) {
+  const int t = blockIdx.x;
+  const int c = (blockIdx.y * 256 + threadIdx.x) * 8;
+  if (c >= H) return;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int j = 0; j < K; ++j) {
+    const int row = slot_pos[(size_t)t * K + j];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(o + (size_t)row * H + c);
+    float f[8];
+    bf16x8_to_f32(v, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += f[i];
+  }
+  if (has_shared) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(o + (size_t)(KT + t) * H + c);
+    float f[8];
+    bf16x8_to_f32(v, f);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += f[i];
+  }
+  u32x4 out;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = pack2(acc[2 * i], acc[2 * i + 1]);
+  *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) = out;
+}
+
+// One workgroup per row: r = r_in (+ y_add) rounded to bf16; x_out =
+// bf16(r / sqrt(mean(r^2) + eps) * (1 + gamma)) computed from the stored
+// bf16 r.  The sum of squares is reduced in a fixed order.
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
+    const uint16_t* r_in, const uint16_t* __restrict__ y_add, const float* __restrict__ gamma,
+    float eps, uint16_t* r_out, uint16_t* __restrict__ x_out, int H) {
+  __shared__ float s_part[4];
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ss = 0.f;
+  float v[8][8];  // H <= 16384: at most 8 chunks of 8 columns per thread
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    const int c = (ch * 256 + threadIdx.x) * 8;
+    if (c < H) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(r_in + (size_t)t * H + c);
+      float f[8];
+      bf16x8_to_f32(a, f);
+      if (y_add) {
+        const u32x4 b = *reinterpret_cast<const u32x4*>(y_add + (size_t)t * H + c);
+        float fb[8];
+        bf16x8_to_f32(b, fb);
+        u32x4 pk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pk[i] = pack2(f[2 * i] + fb[2 * i], f[2 * i + 1] + fb[2 * i + 1]);
+        if (r_out) *reinterpret_cast<u32x4*>(r_out + (size_t)t * H + c) = pk;
+        bf16x8_to_f32(pk, f);  // continue from the stored bf16 value
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[ch][i] = f[i];
+        ss += f[i] * f[i];
+      }
+    }
+  }
+  if (!x_out) return;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int ch = 0; ch < 8; ++ch) {
+    const int c = (ch * 256 + threadIdx.x) * 8;
+    if (c < H) {
+      u32x4 pk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float g0 = 1.f, g1 = 1.f;
+        if (gamma) {
+          g0 += gamma[c + 2 * i];
+          g1 += gamma[c + 2 * i + 1];
+        }
+        pk[i] = pack2(v[ch][2 * i] * inv * g0, v[ch][2 * i + 1] * inv * g1);
+      }
+      *reinterpret_cast<u32x4*>(x_out + (size_t)t * H + c) = pk;
+    }
+  }
+}
+
+hipError_t launch_combine(const Plan& p, const uint16_t* o, const int32_t* slot_pos,
+                          uint16_t* y, hipStream_t s) {
+  dim3 grid(p.T, (p.H / 8 + 255) / 256);
+  hipLaunchKernelGGL(combine_kernel, grid, dim3(256), 0, s, o, slot_pos, y, p.T, p.H, p.K, p.KT,
+                     p.Is > 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_residual_rmsnorm(int T, int H, const uint16_t* r_in, const uint16_t* y_add,
+                                   const float* gamma, float eps, uint16_t* r_out,
+                                   uint16_t* x_out, hipStream_t s) {
+  hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(T), dim3(256), 0, s, r_in, y_add, gamma, eps,
+                     r_out, x_out, H);
+  return hipGetLastError();
+}
+
+}  // namespace smoe

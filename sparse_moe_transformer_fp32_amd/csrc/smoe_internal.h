@@ -1,0 +1,93 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace smoe {
+
+// ---------------------------------------------------------------- device types
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// One row block of the grouped GEMMs: `n_rows` consecutive rows (in the
+// expert-contiguous row order) that belong to `group` (an expert id, or E for
+// the shared expert), starting at global row `row_start`.
+struct RowBlock {
+  int32_t group;
+  int32_t row_start;
+  int32_t n_rows;
+  int32_t pad;
+};
+
+// ---------------------------------------------------------------- tiling plan
+// Every size the launches use is a pure function of the layer sizes, so the
+// workspace size, the dispatch kernel and the GEMM launches agree.
+struct Plan {
+  int32_t T, H, E, K, I, Is;
+  int32_t KT;            // T*K routed rows
+  int32_t rows_total;    // KT + (Is > 0 ? T : 0)
+  int32_t route_tok;     // tokens per router tile (16 or 64)
+  int32_t route_splits;  // split of H across router workgroups
+  int32_t nb;            // 16-token column blocks per GEMM tile
+  int32_t bn;            // rows per row block = 16 * nb
+  int32_t rb_max;        // upper bound on row blocks
+  int32_t ksplit_gu;     // waves splitting K in the gate/up GEMM
+  int32_t ksplit_dn;     // waves splitting K in the down GEMM
+  int32_t gu_rows_wg;    // intermediate rows per gate/up workgroup
+  int32_t dn_rows_wg;    // hidden rows per down workgroup
+  int32_t gu_tiles;      // workgroups per row block (gate/up)
+  int32_t dn_tiles;      // workgroups per row block (down)
+  // workspace byte offsets
+  size_t ws_partial, ws_topk_idx, ws_topk_w, ws_counts, ws_offsets, ws_perm,
+      ws_slot, ws_row_token, ws_row_w, ws_rb, ws_nrb, ws_h, ws_o, ws_total;
+};
+
+void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p);
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.
+hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
+                               float* partial, hipStream_t s);
+hipError_t launch_route_topk(const Plan& p, const float* partial, const float* bias,
+                             float scale, int norm, int bias_in_weights, int32_t* topk_idx,
+                             float* topk_w, float* keys, float* scores, hipStream_t s);
+hipError_t launch_dispatch(const Plan& p, const int32_t* topk_idx, const float* topk_w,
+                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
+                           int32_t* slot_pos, int32_t* row_token, float* row_w,
+                           RowBlock* rb, int32_t* n_rb, hipStream_t s);
+
+struct GateUpArgs {
+  const uint16_t* wg;   // [E, I, H]
+  const uint16_t* wu;   // [E, I, H]
+  const uint16_t* sg;   // [Is, H]  (shared)
+  const uint16_t* su;   // [Is, H]
+  const uint16_t* x;    // [T, H]
+  const int32_t* row_token;
+  const RowBlock* rb;
+  const int32_t* n_rb;
+  uint16_t* h;          // routed [KT, I] then shared [T, Is]
+  float limit, limit_shared;
+};
+struct DownArgs {
+  const uint16_t* wd;   // [E, H, I]
+  const uint16_t* sd;   // [H, Is]
+  const uint16_t* h;
+  const float* row_w;
+  const RowBlock* rb;
+  const int32_t* n_rb;
+  uint16_t* o;          // [rows_total, H]
+};
+hipError_t launch_gate_up(const Plan& p, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_down(const Plan& p, const DownArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const Plan& p, const uint16_t* o, const int32_t* slot_pos,
+                          uint16_t* y, hipStream_t s);
+hipError_t launch_residual_rmsnorm(int T, int H, const uint16_t* r_in, const uint16_t* y_add,
+                                   const float* gamma, float eps, uint16_t* r_out,
+                                   uint16_t* x_out, hipStream_t s);
+
+}  // namespace smoe

@@ -1,0 +1,232 @@
+"""HIP path vs CPU oracle, element by element, through the C-ABI (gfx950 GPU).
+
+Small cases cover every tiling variant (row-block heights 16/32/64/128,
+split-K 1/2/4), ragged tails, T=1, K=1, K=E, E not a multiple of 64, the
+largest E and K, no shared expert, the SwiGLU clamp and the alternative bias
+reading.  Flash-shaped cases run the same launch configuration as the
+benchmark: full outputs at T=16 and sampled rows at T=4096/8192.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_moe_transformer_fp32_amd import binding as B
+from sparse_moe_transformer_fp32_amd.inputs import WORKLOADS, make_inputs, random_tiny
+from tests.parity import LazyStack, check_output, check_routing, gpu_routing_np, host_f64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _to_gpu_bf16(inp):
+    """Small CPU-drawn case -> device tensors; x and expert weights cast to
+    bf16 (round to nearest even), router kept fp32."""
+    L = inp.layers[0]
+    bf = lambda t: None if t is None else t.to(torch.bfloat16).to(DEV).contiguous()
+    f32 = lambda t: t.to(torch.float32).to(DEV).contiguous()
+    return dict(x=bf(inp.x), Wr=f32(inp.router_w), b=f32(inp.router_b), wg=bf(L.w_gate),
+                wu=bf(L.w_up), wd=bf(L.w_down), sg=bf(L.ws_gate), su=bf(L.ws_up),
+                sd=bf(L.ws_down))
+
+
+def _run(g, K, keys=True, **opts):
+    y, r, layer = B.forward(g["x"], g["Wr"], g["b"], g["wg"], g["wu"], g["wd"], g["sg"], g["su"],
+                            g["sd"], K=K, routing=True, keys=keys, **opts)
+    torch.cuda.synchronize()
+    return host_f64(y), gpu_routing_np(r), layer
+
+
+def _oracle_full(g, K, sel=None, **kw):
+    f = {k: (None if v is None else host_f64(v)) for k, v in g.items()}
+    return oracle.moe_layer(f["x"], f["Wr"], f["b"], f["wg"], f["wu"], f["wd"], f["sg"], f["su"],
+                            f["sd"], K=K, sel=sel, return_parts=True, **kw)
+
+
+def _check_case(g, K, **opts):
+    print(f"case T={g['x'].shape[0]} H={g['x'].shape[1]} E={g['Wr'].shape[0]} K={K} "
+          f"I={g['wg'].shape[1]} Is={0 if g['sg'] is None else g['sg'].shape[0]} {opts}", flush=True)
+    y, rg, _ = _run(g, K, **opts)
+    scale = opts.get("route_scale", 3.0)
+    norm = opts.get("norm_topk", True)
+    biw = opts.get("bias_in_weights", False)
+    okw = dict(scale=scale, norm=norm, bias_in_weights=biw,
+               limit=opts.get("swiglu_limit", 0.0), limit_shared=opts.get("swiglu_limit_shared", 0.0))
+    ref = _oracle_full(g, K, **okw)
+    E = g["Wr"].shape[0]
+    check_routing(rg, ref, K, E, host_f64(g["b"]), scale, norm, biw)
+    # the oracle on the GPU's selection (identical except for near ties)
+    ref2 = _oracle_full(g, K, sel=rg["topk_idx"].astype(np.int64), **okw)
+    return check_output(y, ref2["y"])
+
+
+def _small(seed, T, H, E, K, I, Is, bias_std=0.1, w_std=0.05):
+    return _to_gpu_bf16(random_tiny(seed, T, H, E, K, I, Is, bias_std=bias_std, w_std=w_std))
+
+
+def test_tiny_workload():
+    g = _to_gpu_bf16(make_inputs(WORKLOADS["tiny"]))
+    _check_case(g, 2)
+
+
+SMALL = {  # name: (seed, T, H, E, K, I, Is)
+    "ragged_nb1_ksplit2": (101, 37, 384, 40, 6, 192, 128),
+    "nb2": (102, 100, 256, 8, 2, 128, 64),
+    "nb4": (103, 200, 256, 8, 2, 128, 128),
+    "nb8": (104, 300, 256, 8, 2, 128, 128),
+    "nb8_fallback_nb4": (105, 300, 384, 8, 2, 192, 64),
+    "no_shared": (106, 50, 256, 16, 4, 64, 0),
+    "T1": (107, 1, 256, 16, 4, 64, 64),
+    "K1": (108, 40, 256, 16, 1, 64, 64),
+    "K_eq_E": (109, 20, 256, 8, 8, 64, 64),
+    "E100": (110, 33, 256, 100, 8, 64, 64),
+    "E1024_K16": (111, 20, 256, 1024, 16, 64, 64),
+    "I_ne_Is": (112, 70, 256, 12, 3, 128, 192),
+    "long_ragged_nb8": (113, 1000, 256, 6, 2, 128, 128),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_cases(name):
+    _check_case(_small(*SMALL[name]), SMALL[name][4])
+
+
+def test_options_clamp_and_biased_weights():
+    g = _small(120, 60, 256, 16, 4, 64, 64, w_std=0.3)
+    _check_case(g, 4, swiglu_limit=0.5, swiglu_limit_shared=0.7)
+    _check_case(g, 4, bias_in_weights=True)
+    _check_case(g, 4, norm_topk=False, route_scale=2.5)
+
+
+def test_bias_forcing_selects_the_forced_set():
+    g = _small(121, 64, 256, 32, 4, 64, 64)
+    forced = torch.tensor([3, 9, 17, 30])
+    b = torch.zeros(32)
+    b[forced] = 10.0
+    g["b"] = b.to(DEV)
+    y, rg, _ = _run(g, 4)
+    assert (rg["topk_idx"] == forced.numpy()[None]).all()
+    assert (rg["counts"][forced.numpy()] == 64).all() and rg["counts"].sum() == 256
+
+
+def test_all_ties_take_lowest_indices():
+    g = _small(122, 16, 256, 20, 5, 64, 64, bias_std=0.0)
+    g["Wr"] = torch.zeros_like(g["Wr"])
+    y, rg, _ = _run(g, 5)
+    assert (rg["topk_idx"] == np.arange(5)[None]).all()
+    assert np.all(rg["topk_w"] == np.float32(3.0) * np.float32(0.5) / np.float32(2.5))
+
+
+def test_deterministic_and_permutation_equivariant():
+    g = _small(123, 96, 512, 24, 4, 128, 128)
+    y1, r1, _ = _run(g, 4)
+    y2, r2, _ = _run(g, 4)
+    assert np.array_equal(y1, y2)
+    for k in r1:
+        assert np.array_equal(r1[k], r2[k])
+    p = torch.randperm(96, generator=torch.Generator().manual_seed(0))
+    gp = dict(g, x=g["x"][p.to(DEV)].contiguous())
+    y3, r3, _ = _run(gp, 4)
+    assert np.array_equal(y3, y1[p.numpy()])
+    assert np.array_equal(r3["topk_idx"], r1["topk_idx"][p.numpy()])
+
+
+# ---------------------------------------------------------------- Flash shape
+def _flash(wl_name, T=None):
+    inp = make_inputs(WORKLOADS[wl_name], device=DEV, T=T)
+    L = inp.layers[0]
+    return dict(x=inp.x, Wr=inp.router_w, b=inp.router_b, wg=L.w_gate, wu=L.w_up, wd=L.w_down,
+                sg=L.ws_gate, su=L.ws_up, sd=L.ws_down), inp
+
+
+def _flash_check(wl_name, n_sample=None, T=None):
+    g, inp = _flash(wl_name, T)
+    K = inp.wl.K
+    Tn = g["x"].shape[0]
+    print(f"flash case {wl_name} T={Tn}", flush=True)
+    y, rg, _ = _run(g, K)
+    x64 = host_f64(g["x"])
+    Wr, b = host_f64(g["Wr"]), host_f64(g["b"])
+    ref_route = oracle.route(x64, Wr, b, K)
+    check_routing(rg, ref_route, K, inp.wl.E, b)
+    rows = np.arange(Tn)
+    if n_sample and n_sample < Tn:
+        rng = np.random.default_rng(inp.wl.seed)
+        rows = np.unique(np.concatenate([[0, Tn - 1], rng.choice(Tn, n_sample - 2, replace=False)]))
+    sel = rg["topk_idx"].astype(np.int64)[rows]
+    yref = oracle.moe_layer(x64[rows], Wr, b, LazyStack(g["wg"]), LazyStack(g["wu"]),
+                            LazyStack(g["wd"]), host_f64(g["sg"]), host_f64(g["su"]),
+                            host_f64(g["sd"]), K=K, sel=sel)
+    res = check_output(y[rows], yref)
+    print(f"  rows={len(rows)} max_rel={res[0]:.3e} l2_rel={res[1]:.3e}", flush=True)
+    return rg
+
+
+def test_flash_decode_full():
+    rg = _flash_check("decode")
+    assert rg["counts"].sum() == 16 * 8
+
+
+def test_flash_prefill_sampled():
+    _flash_check("prefill", n_sample=24)
+
+
+def test_flash_skew_sampled():
+    rg = _flash_check("skew", n_sample=16)
+    from sparse_moe_transformer_fp32_amd.inputs import boosted_experts
+    boost = boosted_experts(WORKLOADS["skew"])
+    share = rg["counts"][boost].sum() / rg["counts"].sum()
+    print(f"  share of slots on the 29 boosted experts: {share:.3f}", flush=True)
+    assert share > 0.99
+
+
+def test_flash_skew_mild_sampled():
+    rg = _flash_check("skew_mild", n_sample=16)
+    from sparse_moe_transformer_fp32_amd.inputs import boosted_experts
+    boost = boosted_experts(WORKLOADS["skew_mild"])
+    share = rg["counts"][boost].sum() / rg["counts"].sum()
+    print(f"  share of slots on the 29 boosted experts: {share:.3f}", flush=True)
+    assert 0.3 < share < 0.8
+
+
+# ---------------------------------------------------------------- RMSNorm glue
+def test_residual_rmsnorm_matches_oracle():
+    gen = torch.Generator().manual_seed(7)
+    T, H = 50, 1152
+    r = (torch.randn(T, H, generator=gen) * 3).to(torch.bfloat16).to(DEV)
+    yv = torch.randn(T, H, generator=gen).to(torch.bfloat16).to(DEV)
+    gamma = (torch.randn(H, generator=gen) * 0.1).to(DEV)
+    r_out, x_out = B.residual_rmsnorm(r, yv, gamma, eps=1e-6)
+    torch.cuda.synchronize()
+    r_ref = host_f64(r) + host_f64(yv)
+    r_got = host_f64(r_out)
+    assert np.abs(r_got - r_ref).max() <= np.abs(r_ref).max() * 2 ** -8
+    x_ref = oracle.rmsnorm(r_got, 1e-6, host_f64(gamma))
+    check_output(host_f64(x_out), x_ref, "rmsnorm")
+    assert np.abs(host_f64(x_out) - x_ref).max() <= np.abs(x_ref).max() * 2 ** -7
+    # norm only, in place residual
+    _, x2 = B.residual_rmsnorm(r, None, None, eps=1e-6)
+    torch.cuda.synchronize()
+    check_output(host_f64(x2), oracle.rmsnorm(host_f64(r), 1e-6), "rmsnorm-only")
+
+
+def test_chain_teacher_forced_small():
+    """Three chained small layers; each GPU step is checked against the
+    oracle fed the GPU's own input of that step."""
+    T, H, E, K, I, Is = 80, 256, 16, 4, 64, 64
+    layers = [_small(130 + i, T, H, E, K, I, Is) for i in range(3)]
+    r = layers[0]["x"]
+    x = None
+    for li, g in enumerate(layers):
+        _, x = B.residual_rmsnorm(r, None, None, eps=1e-6)
+        gx = dict(g, x=x)
+        y, rg, _ = _run(gx, K)
+        ref = _oracle_full(gx, K, sel=rg["topk_idx"].astype(np.int64))
+        check_output(y, ref["y"], f"layer {li}")
+        check_output(host_f64(x), oracle.rmsnorm(host_f64(r), 1e-6), f"norm {li}")
+        r_new, _ = B.residual_rmsnorm(r, torch.from_numpy(y).to(torch.bfloat16).to(DEV), None,
+                                      want_x=False)
+        torch.cuda.synchronize()
+        check_output(host_f64(r_new), host_f64(r) + y, f"residual {li}")
+        r = r_new

@@ -24,6 +24,7 @@ def _pins_pass():
         P.test_p9_single_row_textbook,
         P.test_rmsnorm_closed_forms,
         P.test_chain_closed_forms,
+        P.test_swiglu_limit_closed_forms,
     ]
     for c in checks:
         try:
@@ -82,17 +83,28 @@ def _weights_from_biased(s, sel, scale=3.0, norm=True, bias=None, bias_in_weight
     return _orig_rw(s, sel, scale, norm, bias, True)
 
 
-def _ffn_down_transposed(xr, Wg, Wu, Wd, return_hidden=False):
+def _ffn_down_transposed(xr, Wg, Wu, Wd, return_hidden=False, **kw):
     Wd = np.asarray(Wd)
     if Wd.shape[0] == Wd.shape[1]:
         Wd = Wd.T
     else:
         raise ValueError("shape mismatch from the transposed operand")
-    return _orig_ffn(xr, Wg, Wu, Wd, return_hidden)
+    return _orig_ffn(xr, Wg, Wu, Wd, return_hidden, **kw)
 
 
-def _ffn_gate_up_swapped(xr, Wg, Wu, Wd, return_hidden=False):
-    return _orig_ffn(xr, Wu, Wg, Wd, return_hidden)
+def _ffn_gate_up_swapped(xr, Wg, Wu, Wd, return_hidden=False, **kw):
+    return _orig_ffn(xr, Wu, Wg, Wd, return_hidden, **kw)
+
+
+def _ffn_clamp_both_sides(xr, Wg, Wu, Wd, return_hidden=False, limit=0.0):
+    if limit <= 0:
+        return _orig_ffn(xr, Wg, Wu, Wd, return_hidden)
+    xr = np.asarray(xr, np.float64)
+    g = np.clip(xr @ np.asarray(Wg, np.float64).T, -limit, limit)
+    u = np.clip(xr @ np.asarray(Wu, np.float64).T, -limit, limit)
+    h = g / (1.0 + np.exp(-g)) * u
+    o = h @ np.asarray(Wd, np.float64).T
+    return (o, h) if return_hidden else o
 
 
 def _dispatch_descending_rows(sel, E):
@@ -142,6 +154,7 @@ MUTATIONS = {
     "rmsnorm_wrong": ("rmsnorm", _rms_no_eps_mean_abs),
     "rmsnorm_gain_not_centred": ("rmsnorm", _rms_gain_not_centred),
     "router_rows_reversed": ("router_logits", _logits_transposed_router),
+    "clamp_gate_both_sides": ("swiglu_ffn", _ffn_clamp_both_sides),
 }
 
 

@@ -290,3 +290,23 @@ def test_bf16_decode_exact():
     assert np.array_equal(got, vals.to(torch.bfloat16).double().numpy())
     assert oracle.bf16_bits_to_f64(np.array([0x3F80], np.uint16))[0] == 1.0
     assert oracle.bf16_bits_to_f64(np.array([0xC020], np.uint16))[0] == -2.5
+
+
+# SwiGLU clamp (reading A17): hand values and the no-op limit ----------------
+def test_swiglu_limit_closed_forms():
+    x = np.array([[1.0]])
+    Wd = np.array([[1.0]])
+    # g = 9 -> clamped to 7; u = -12 -> clamped to -7
+    o = oracle.swiglu_ffn(x, np.array([[9.0]]), np.array([[-12.0]]), Wd, limit=7.0)
+    assert abs(o[0, 0] - 7.0 / (1.0 + math.exp(-7.0)) * -7.0) < 1e-14
+    # the gate is clamped from above only: g = -9 stays
+    o = oracle.swiglu_ffn(x, np.array([[-9.0]]), np.array([[3.0]]), Wd, limit=7.0)
+    assert abs(o[0, 0] - (-9.0) / (1.0 + math.exp(9.0)) * 3.0) < 1e-15
+    # a limit above every activation changes nothing
+    inp = random_tiny(71, 6, 10, 8, 2, 4, 5)
+    a = _args(inp)
+    y0 = oracle.moe_layer(*a, K=2)
+    y1 = oracle.moe_layer(*a, K=2, limit=1e6, limit_shared=1e6)
+    assert np.array_equal(y0, y1)
+    y2 = oracle.moe_layer(*a, K=2, limit=1e-3, limit_shared=1e-3)
+    assert not np.allclose(y0, y2)
