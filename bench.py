@@ -1,0 +1,319 @@
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode]
+
+One step = one full pass of the layer (router, top-K, dispatch, grouped
+gate/up + SwiGLU, grouped down + weights, combine) over one batch of seeded
+synthetic inputs already resident in HBM.  The default workload is the
+Step-3.5-Flash decode batch (T=16 tokens: 4 sequences x (1 + 3 MTP drafts)),
+the configuration the headline metric is quoted on; a prefill pass at
+T=4096 is reported beside it (`prefill` object) because the metric names
+both.  Prints ONE JSON line.
+
+roofline: the dominant kernel (gate/up + SwiGLU) timed with HIP events that
+the library records around it on its own stream, against its algorithmic
+bytes (decode, HBM bound) or FLOPs (prefill).
+cpu_baseline: the float64 CPU oracle timed on the host cores on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def _hip():
+    """The HIP runtime already loaded in this process (the one torch and the
+    library share)."""
+    maps = open("/proc/self/maps").read()
+    paths = sorted(set(re.findall(r"(/\S*libamdhip64\.so\S*)", maps)))
+    lib = ctypes.CDLL(paths[0] if paths else "libamdhip64.so")
+    lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return lib
+
+
+class StageTimer:
+    """Per-step arrays of begin/end events for every library stage."""
+
+    def __init__(self, hip, n_steps: int, n_stages: int):
+        self.hip = hip
+        self.n_stages = n_stages
+        self.arrays = []
+        for _ in range(n_steps):
+            arr = (ctypes.c_void_p * (2 * n_stages))()
+            for i in range(2 * n_stages):
+                ev = ctypes.c_void_p()
+                assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+                arr[i] = ev
+            self.arrays.append(arr)
+
+    def stage_ms(self):
+        """Mean duration (ms) of each stage over the recorded steps."""
+        out = []
+        for s in range(self.n_stages):
+            tot = 0.0
+            for arr in self.arrays:
+                ms = ctypes.c_float()
+                assert self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * s], arr[2 * s + 1]) == 0
+                tot += ms.value
+            out.append(tot / len(self.arrays))
+        return out
+
+    def close(self):
+        for arr in self.arrays:
+            for ev in arr:
+                self.hip.hipEventDestroy(ev)
+
+
+def _src_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+GEMM_SOURCES = ["sparse_moe_transformer_fp32_amd/csrc/expert_gemm.hip",
+                "sparse_moe_transformer_fp32_amd/csrc/api.cpp"]
+
+
+def _traffic(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel_key)
+    if not rec or rec.get("source_sha") != _src_sha(GEMM_SOURCES):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def layer_work(wl, counts):
+    """Algorithmic bytes and FLOPs of one layer call, and of its gate/up
+    kernel, from the measured expert counts."""
+    T, H, E, K, I, Is = wl.T, wl.H, wl.E, wl.K, wl.I, wl.Is
+    n_act = int((counts > 0).sum())
+    rows = T * K + (T if Is else 0)
+    w_gu = (n_act * 2 * I * H + (2 * Is * H if Is else 0)) * 2
+    w_dn = (n_act * H * I + (H * Is if Is else 0)) * 2
+    gu_bytes = w_gu + T * H * 2 + (T * K * I + T * Is) * 2          # weights, x, h
+    layer_bytes = w_gu + w_dn + E * H * 4 + E * 4 + 2 * T * H * 2    # weights, router, x, y
+    gu_flops = 2 * (T * K * 2 * I * H + (T * 2 * Is * H if Is else 0))
+    layer_flops = 2 * (T * K * 3 * I * H + (T * 3 * Is * H if Is else 0))
+    router_flops = 2 * T * E * H
+    return dict(n_active=n_act, rows=rows, gu_bytes=gu_bytes, layer_bytes=layer_bytes,
+                gu_flops=gu_flops, layer_flops=layer_flops, router_flops=router_flops)
+
+
+def run_layer_bench(wl_name, steps, warmup, device="cuda"):
+    import torch
+    from sparse_moe_transformer_fp32_amd import binding as B
+    from sparse_moe_transformer_fp32_amd.inputs import WORKLOADS, make_inputs
+
+    wl = WORKLOADS[wl_name]
+    inp = make_inputs(wl, device=device)
+    layers = []
+    for li, L in enumerate(inp.layers):
+        layers.append(B.MoELayer(inp.router_ws[li], inp.router_bs[li], L.w_gate, L.w_up, L.w_down,
+                                 L.ws_gate, L.ws_up, L.ws_down, K=wl.K, T_max=wl.T,
+                                 route_scale=wl.route_scale, norm_topk=wl.norm_topk))
+    T = wl.T
+    x = inp.x
+    routing = B.alloc_routing(T, wl.E, wl.K, device)
+    nl = len(layers)
+    y = torch.empty_like(x)
+    r_buf = [torch.empty_like(x) for _ in range(2)]
+    xn = torch.empty_like(x)
+
+    def step():
+        if nl == 1:
+            layers[0].forward(x, y, routing)
+            return
+        # pre-norm residual stream through chained layers
+        r = x
+        for li, lay in enumerate(layers):
+            B.residual_rmsnorm(r, None, None, 1e-6, None, xn, want_r=False)
+            lay.forward(xn, y, routing if li == nl - 1 else None)
+            r_next = r_buf[li % 2]
+            B.residual_rmsnorm(r, y, None, 1e-6, r_next, None, want_x=False)
+            r = r_next
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hip = _hip()
+    timer = StageTimer(hip, steps, len(B.STAGES))
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(steps):
+        B.set_stage_events(timer.arrays[k])
+        step()
+    B.set_stage_events(None)
+    stop.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    gpu_ms = start.elapsed_time(stop) / steps
+    stage_ms = timer.stage_ms()
+    timer.close()
+    counts = routing["counts"].cpu().numpy()
+    return dict(wl=wl, inp=inp, layers=layers, routing=routing, counts=counts, wall_ms=wall_ms,
+                gpu_ms=gpu_ms, stage_ms=dict(zip(B.STAGES, stage_ms)), n_layers=nl)
+
+
+def cpu_baseline(res, max_tokens=16, budget_s=30.0):
+    """Time the float64 oracle on the host on up to `max_tokens` tokens of the
+    workload (weights copied to host memory first; the timed region is the
+    oracle call alone, including its bf16 -> float64 widening)."""
+    import numpy as np
+    import oracle
+    from sparse_moe_transformer_fp32_amd.inputs import bf16_bits
+
+    wl, inp = res["wl"], res["inp"]
+    L = inp.layers[0]
+    rows = np.arange(min(max_tokens, wl.T))
+    xs = oracle.bf16_bits_to_f64(bf16_bits(inp.x[: len(rows)])).reshape(len(rows), wl.H)
+    Wr = inp.router_ws[0].double().cpu().numpy()
+    b = inp.router_bs[0].double().cpu().numpy()
+    sel = oracle.select_topk(oracle.selection_keys(oracle.router_scores(oracle.router_logits(xs, Wr)), b), wl.K)
+    need = np.unique(sel)
+
+    class HostStack:
+        def __init__(self, t):
+            self.bits = {int(e): bf16_bits(t[int(e)]) for e in need}
+
+        def __getitem__(self, e):
+            return oracle.bf16_bits_to_f64(self.bits[int(e)])
+
+    wg, wu, wd = HostStack(L.w_gate), HostStack(L.w_up), HostStack(L.w_down)
+    sh = [oracle.bf16_bits_to_f64(bf16_bits(t)).reshape(tuple(t.shape)) for t in
+          (L.ws_gate, L.ws_up, L.ws_down)]
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    oracle.moe_layer(xs, Wr, b, wg, wu, wd, *sh, K=wl.K)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {wl.T} tokens of the {wl.name} batch, one layer, float64 "
+                      f"NumPy oracle ({dt:.2f} s), weights pre-staged in host memory"}
+
+
+def roofline_obj(bound, achieved, peak, unit, traffic):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "prefill", "skew", "skew_mild", "long", "tiny"])
+    ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 side measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: there is no multi-GPU path; --gpus must be 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    torch.cuda.set_device(0)
+    res = run_layer_bench(args.workload, args.steps, args.warmup)
+    wl = res["wl"]
+    work = layer_work(wl, res["counts"])
+    ms = res["wall_ms"]
+    tok_s = wl.T / (ms / 1e3)
+    gu_ms = res["stage_ms"]["gate_up"]
+    nl = res["n_layers"]
+    if wl.T <= 64:   # weight streaming: HBM bound
+        rf = roofline_obj("hbm", work["gu_bytes"] / (gu_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
+                          _traffic(f"gate_up:{wl.name}"))
+    else:
+        rf = roofline_obj("mfma", work["gu_flops"] / (gu_ms * 1e-3) / 1e12,
+                          MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", _traffic(f"gate_up:{wl.name}"))
+    layer_ms = ms / nl
+    line = {
+        "metric": "MoE-layer tokens/s + % roofline (HBM GB/s @T=16, MFMA TFLOP/s @T=4096)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{wl.name}: T={wl.T} tokens, H={wl.H}, E={wl.E} routed top-{wl.K} + "
+                        f"{'1 shared' if wl.Is else 'no shared'} expert, I={wl.I}, Is={wl.Is}, "
+                        f"{nl} layer(s), bf16 experts, fp32 sigmoid router",
+            "T": wl.T, "H": wl.H, "E": wl.E, "K": wl.K, "I": wl.I, "Is": wl.Is, "layers": nl,
+            "seed": wl.seed,
+        },
+        "roofline": rf,
+        "layer": {
+            "gpu_ms_per_step": round(res["gpu_ms"], 4),
+            "active_experts": work["n_active"],
+            "algorithmic_bytes": work["layer_bytes"],
+            "hbm_gbs": round(work["layer_bytes"] / (layer_ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(work["layer_bytes"] / (layer_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bf16_tflops": round(work["layer_flops"] / (layer_ms * 1e-3) / 1e12, 2),
+            "stage_ms": {k: round(v, 4) for k, v in res["stage_ms"].items()},
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(res)
+    if args.workload == "decode" and not args.no_prefill:
+        del res
+        torch.cuda.empty_cache()
+        pre = run_layer_bench("prefill", max(5, args.steps // 5), 3)
+        pw = layer_work(pre["wl"], pre["counts"])
+        pms = pre["wall_ms"]
+        pgu = pre["stage_ms"]["gate_up"]
+        line["prefill"] = {
+            "workload": "prefill: T=4096 tokens, Flash shape, near-uniform routing",
+            "tokens_per_s": round(4096 / (pms / 1e3), 1),
+            "ms_per_step": round(pms, 4),
+            "bf16_tflops": round(pw["layer_flops"] / (pms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(pw["layer_flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(pw["layer_bytes"] / (pms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(pw["layer_bytes"] / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "roofline_gate_up": roofline_obj("mfma", pw["gu_flops"] / (pgu * 1e-3) / 1e12,
+                                             MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
+                                             _traffic("gate_up:prefill")),
+            "gate_up_hbm_gbs": round(pw["gu_bytes"] / (pgu * 1e-3) / 1e9, 1),
+            "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
+        }
+        del pre
+        torch.cuda.empty_cache()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

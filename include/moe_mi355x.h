@@ -133,6 +133,15 @@ typedef struct {
  * (shared rows by 1). */
 typedef struct { size_t h, o, total; } moe_ws_layout;
 
+/* Stages of moe_forward, in launch order (moe_route runs the first three). */
+#define MOE_STAGE_ROUTE_LOGITS 0
+#define MOE_STAGE_ROUTE_TOPK 1
+#define MOE_STAGE_DISPATCH 2
+#define MOE_STAGE_GATE_UP 3
+#define MOE_STAGE_DOWN 4
+#define MOE_STAGE_COMBINE 5
+#define MOE_N_STAGES 6
+
 /* ABI version of the library (MOE_ABI_VERSION of the header it was built
  * from). */
 int32_t moe_abi_version(void);
@@ -190,6 +199,15 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
 moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
                                 const uint16_t* y_add, const float* gamma, float eps,
                                 uint16_t* r_out, uint16_t* x_out, hipStream_t stream);
+
+/* Per-stage timing hook for benchmarks and profilers (thread-local, host).
+ * `events` is a host array of 2*MOE_N_STAGES hipEvent_t created by the
+ * caller (hipEventCreate); while it is set, every moe_route / moe_forward on
+ * this thread records events[2*i] just before and events[2*i+1] just after
+ * stage i on the call's stream, so hipEventElapsedTime(events[2*i],
+ * events[2*i+1]) is that kernel's duration.  Pass NULL (n_events ignored) to
+ * stop.  Returns MOE_ERR_SHAPE unless n_events == 2*MOE_N_STAGES. */
+moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events);
 
 #ifdef __cplusplus
 }

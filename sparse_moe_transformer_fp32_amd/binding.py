@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
                 -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_DEVICE"}
 
 EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
-            "moe_route", "moe_forward", "moe_residual_rmsnorm"]
+            "moe_route", "moe_forward", "moe_residual_rmsnorm", "moe_set_stage_events"]
+STAGES = ["route_logits", "route_topk", "dispatch", "gate_up", "down", "combine"]
 
 _vp = ctypes.c_void_p
 
@@ -94,6 +95,8 @@ def load() -> ctypes.CDLL:
     lib.moe_residual_rmsnorm.restype = ctypes.c_int
     lib.moe_residual_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
                                          ctypes.c_float, _vp, _vp, _vp]
+    lib.moe_set_stage_events.restype = ctypes.c_int
+    lib.moe_set_stage_events.argtypes = [_vp, ctypes.c_int32]
     v = lib.moe_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH}: ABI version {v}, binding expects {ABI_VERSION}")
@@ -265,6 +268,16 @@ def forward(x, router_w, router_b, w_gate, w_up, w_down, ws_gate=None, ws_up=Non
     r = alloc_routing(x.shape[0], layer.E, K, x.device, keys) if routing else None
     y = layer.forward(x, routing=r)
     return (y, r, layer) if routing else y
+
+
+def set_stage_events(events_array) -> None:
+    """Install (or with None, remove) the per-stage timing events: a ctypes
+    array of 2 * len(STAGES) hipEvent_t handles (see moe_set_stage_events)."""
+    lib = load()
+    if events_array is None:
+        _check(lib.moe_set_stage_events(None, 0))
+    else:
+        _check(lib.moe_set_stage_events(ctypes.cast(events_array, _vp), len(events_array)))
 
 
 def residual_rmsnorm(r_in: torch.Tensor, y_add: Optional[torch.Tensor] = None,

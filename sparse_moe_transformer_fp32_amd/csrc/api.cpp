@@ -13,6 +13,19 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local hipEvent_t* g_stage_events = nullptr;
+
+// Records the stage's begin/end event when the timing hook is set.
+struct StageMark {
+  int stage;
+  hipStream_t s;
+  StageMark(int st, hipStream_t stream) : stage(st), s(stream) {
+    if (g_stage_events) (void)hipEventRecord(g_stage_events[2 * stage], s);
+  }
+  ~StageMark() {
+    if (g_stage_events) (void)hipEventRecord(g_stage_events[2 * stage + 1], s);
+  }
+};
 
 moe_status fail(moe_status st, const char* fmt, ...) {
   char buf[512];
@@ -85,13 +98,20 @@ moe_status run_route(const smoe::Plan& p, const moe_opts& o, const uint16_t* x,
                      const moe_router* router, const RouteBufs& rbuf, char* ws, hipStream_t s) {
   float* partial = reinterpret_cast<float*>(ws + p.ws_partial);
   moe_status st;
-  if ((st = launched(smoe::launch_route_logits(p, x, router->W, partial, s), "route_logits")))
-    return st;
-  if ((st = launched(smoe::launch_route_topk(p, partial, router->b, o.route_scale, o.norm_topk,
-                                             o.bias_in_weights, rbuf.topk_idx, rbuf.topk_w,
-                                             rbuf.keys, rbuf.scores, s),
-                     "route_topk")))
-    return st;
+  {
+    StageMark m(MOE_STAGE_ROUTE_LOGITS, s);
+    if ((st = launched(smoe::launch_route_logits(p, x, router->W, partial, s), "route_logits")))
+      return st;
+  }
+  {
+    StageMark m(MOE_STAGE_ROUTE_TOPK, s);
+    if ((st = launched(smoe::launch_route_topk(p, partial, router->b, o.route_scale, o.norm_topk,
+                                               o.bias_in_weights, rbuf.topk_idx, rbuf.topk_w,
+                                               rbuf.keys, rbuf.scores, s),
+                       "route_topk")))
+      return st;
+  }
+  StageMark m(MOE_STAGE_DISPATCH, s);
   return launched(
       smoe::launch_dispatch(p, rbuf.topk_idx, rbuf.topk_w, rbuf.counts, rbuf.offsets, rbuf.perm,
                             rbuf.slot, reinterpret_cast<int32_t*>(ws + p.ws_row_token),
@@ -302,7 +322,10 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
   ga.h = h;
   ga.limit = o.swiglu_limit;
   ga.limit_shared = o.swiglu_limit_shared;
-  if ((st = launched(smoe::launch_gate_up(p, ga, stream), "gate_up"))) return st;
+  {
+    StageMark m(MOE_STAGE_GATE_UP, stream);
+    if ((st = launched(smoe::launch_gate_up(p, ga, stream), "gate_up"))) return st;
+  }
 
   smoe::DownArgs da{};
   da.wd = experts->w_down;
@@ -312,9 +335,26 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
   da.rb = rbl;
   da.n_rb = nrb;
   da.o = ob;
-  if ((st = launched(smoe::launch_down(p, da, stream), "down"))) return st;
+  {
+    StageMark m(MOE_STAGE_DOWN, stream);
+    if ((st = launched(smoe::launch_down(p, da, stream), "down"))) return st;
+  }
+  {
+    StageMark m(MOE_STAGE_COMBINE, stream);
+    if ((st = launched(smoe::launch_combine(p, ob, rb.slot, y, stream), "combine"))) return st;
+  }
+  return ok();
+}
 
-  if ((st = launched(smoe::launch_combine(p, ob, rb.slot, y, stream), "combine"))) return st;
+moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events) {
+  if (!events) {
+    g_stage_events = nullptr;
+    return ok();
+  }
+  if (n_events != 2 * MOE_N_STAGES)
+    return fail(MOE_ERR_SHAPE, "moe_set_stage_events: n_events=%d, expected %d", n_events,
+                2 * MOE_N_STAGES);
+  g_stage_events = events;
   return ok();
 }
 

@@ -115,49 +115,50 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Software pipeline over stages of U k-steps with two register buffers.
+  // Every load is unconditional so the compiler's wait counts let one stage
+  // stream in while the other is multiplied; slots past the end of K re-read
+  // the last valid chunk (in bounds) and skip their MFMAs.
+  const int nsteps = klen / 32;
+  const int nstages = (nsteps + U - 1) / U;
   u32x4 a0[U][FR], b0[U][NB], a1[U][FR], b1[U][NB];
-  auto load = [&](u32x4 (&a)[U][FR], u32x4 (&b)[U][NB], int k) {
+  auto load = [&](u32x4 (&a)[U][FR], u32x4 (&b)[U][NB], int stage) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      const int k = min(stage * U + u, nsteps - 1) * 32;
 #pragma unroll
       for (int f = 0; f < FR; ++f)
-        a[u][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(aptr[f] + k + 32 * u));
+        a[u][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(aptr[f] + k));
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + k + 32 * u);
+      for (int nb = 0; nb < NB; ++nb) b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + k);
     }
   };
-  auto compute = [&](const u32x4 (&a)[U][FR], const u32x4 (&b)[U][NB]) {
+  auto compute = [&](const u32x4 (&a)[U][FR], const u32x4 (&b)[U][NB], int stage) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      if (stage * U + u < nsteps) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int f = 0; f < FR; ++f) acc[f][nb] = mfma16(a[u][f], b[u][nb], acc[f][nb]);
+          for (int f = 0; f < FR; ++f) acc[f][nb] = mfma16(a[u][f], b[u][nb], acc[f][nb]);
+      }
+    }
   };
 
-  constexpr int STEP = 32 * U;
-  const int kmain = (klen / STEP) * STEP;
-  if (kmain > 0) {
-    load(a0, b0, 0);
-    for (int k = 0; k < kmain; k += 2 * STEP) {
-      const bool has1 = k + STEP < kmain;
-      if (has1) load(a1, b1, k + STEP);
-      compute(a0, b0);
-      if (k + 2 * STEP < kmain) load(a0, b0, k + 2 * STEP);
-      if (has1) compute(a1, b1);
-    }
+  load(a0, b0, 0);
+  int st = 0;
+  for (; st + 2 < nstages; st += 2) {
+    load(a1, b1, st + 1);
+    compute(a0, b0, st);
+    load(a0, b0, st + 2);
+    compute(a1, b1, st + 1);
   }
-  for (int k = kmain; k < klen; k += 32) {   // remainder, one k-step at a time
-    u32x4 a[1][FR], b[1][NB];
-#pragma unroll
-    for (int f = 0; f < FR; ++f) a[0][f] = *reinterpret_cast<const u32x4*>(aptr[f] + k);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) b[0][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + k);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int f = 0; f < FR; ++f) acc[f][nb] = mfma16(a[0][f], b[0][nb], acc[f][nb]);
+  if (st + 1 < nstages) {
+    load(a1, b1, st + 1);
+    compute(a0, b0, st);
+    compute(a1, b1, st + 1);
+  } else {
+    compute(a0, b0, st);
   }
 
   if (KSPLIT > 1) {

@@ -104,6 +104,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   if (t >= T) return;
   const int C = (E + 63) >> 6;
 
+  // logits: sum the split-H partial sums in a fixed order; all loads of a
+  // group of four splits are issued before any add
+  float lg[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) lg[c] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 4) {
+    float v[16][4];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int e = min(c * 64 + lane, E - 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        v[c][q] = (c < C && s0 + q < S) ? partial[((size_t)(s0 + q) * T + t) * E + e] : 0.f;
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) lg[c] += v[c][q];
+  }
+
   float key[16], sc[16];
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
@@ -111,8 +131,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     sc[c] = 0.f;
     const int e = c * 64 + lane;
     if (c < C && e < E) {
-      float l = 0.f;
-      for (int s = 0; s < S; ++s) l += partial[((size_t)s * T + t) * E + e];
+      const float l = lg[c];
       const float sg = 1.0f / (1.0f + expf(-l));
       const float kk = sg + bias[e];
       sc[c] = sg;
