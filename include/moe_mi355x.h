@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -98,10 +98,19 @@ typedef struct {
 /* Router: W [E,H] fp32, b [E] fp32 (learned bias, may be all zero). */
 typedef struct { const float* W; const float* b; } moe_router;
 
-/* Routed experts, bf16: w_gate [E,I,H], w_up [E,I,H], w_down [E,H,I]. */
+/* Packed weight layout.  moe_forward reads every expert matrix in the
+ * fragment-packed layout that moe_pack_weights produces from the model's
+ * row-major bf16 matrix W[R][C] (R a multiple of 16, C of 32): 16x32 tiles of
+ * 512 elements, tile (rt, kt) holding rows 16rt..16rt+15 and columns
+ * 32kt..32kt+31 at element offset (rt*(C/32) + kt)*512; inside a tile,
+ * W[16rt + r][32kt + c] sits at offset 8*(16*(c/8) + r) + c%8.  A packed
+ * matrix has the same size as the row-major one. */
+
+/* Routed experts, bf16, PACKED: w_gate E x [I,H], w_up E x [I,H],
+ * w_down E x [H,I] (matrix e at element offset e*I*H). */
 typedef struct { const uint16_t* w_gate; const uint16_t* w_up; const uint16_t* w_down; } moe_experts;
 
-/* Shared expert, bf16: w_gate [Is,H], w_up [Is,H], w_down [H,Is].
+/* Shared expert, bf16, PACKED: w_gate [Is,H], w_up [Is,H], w_down [H,Is].
  * Pass NULL (or set dims.Is = 0) for a layer without a shared expert. */
 typedef struct { const uint16_t* w_gate; const uint16_t* w_up; const uint16_t* w_down; } moe_shared;
 
@@ -186,6 +195,13 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
                        const moe_shared* shared, uint16_t* y,
                        const moe_routing* routing_out, void* ws, size_t ws_bytes,
                        hipStream_t stream);
+
+/* Convert n_mats row-major bf16 matrices [rows, cols] (consecutive in src)
+ * into the packed layout above (consecutive in dst).  Done once when weights
+ * are loaded.  rows must be a multiple of 16, cols of 32; src and dst must
+ * not overlap; both 16-byte aligned.  Asynchronous on `stream`. */
+moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, int32_t rows,
+                            int32_t cols, hipStream_t stream);
 
 /* Glue between chained layers of a pre-norm residual stream (paperlayer.ai
  * summary, App. B: RMSNorm over the summed layer outputs; model card:

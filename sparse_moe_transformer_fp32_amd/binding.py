@@ -15,7 +15,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsmoe_gfx950.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_OPTION = 0, -1, -2, -3
 MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_DEVICE = -4, -5, -6
@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
                 -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_DEVICE"}
 
 EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
-            "moe_route", "moe_forward", "moe_residual_rmsnorm", "moe_set_stage_events"]
+            "moe_route", "moe_forward", "moe_residual_rmsnorm", "moe_set_stage_events",
+            "moe_pack_weights"]
 STAGES = ["route_logits", "route_topk", "dispatch", "gate_up", "down", "combine"]
 
 _vp = ctypes.c_void_p
@@ -95,6 +96,8 @@ def load() -> ctypes.CDLL:
     lib.moe_residual_rmsnorm.restype = ctypes.c_int
     lib.moe_residual_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
                                          ctypes.c_float, _vp, _vp, _vp]
+    lib.moe_pack_weights.restype = ctypes.c_int
+    lib.moe_pack_weights.argtypes = [_vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp]
     lib.moe_set_stage_events.restype = ctypes.c_int
     lib.moe_set_stage_events.argtypes = [_vp, ctypes.c_int32]
     v = lib.moe_abi_version()
@@ -200,12 +203,32 @@ def route(x: torch.Tensor, router_w: torch.Tensor, router_b: torch.Tensor, K: in
     return r
 
 
+def pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Fragment-packed copy (moe_pack_weights) of a row-major bf16 matrix
+    [R, C] or stack of matrices [n, R, C]."""
+    lib = load()
+    _dev(w, "w", torch.bfloat16)
+    if w.dim() == 2:
+        n, R, C = 1, w.shape[0], w.shape[1]
+    elif w.dim() == 3:
+        n, R, C = w.shape
+    else:
+        raise ValueError("pack_weights expects a 2-D or 3-D tensor")
+    if out is None:
+        out = torch.empty_like(w)
+    _dev(out, "out", torch.bfloat16)
+    _check(lib.moe_pack_weights(_ptr(w), _ptr(out), n, R, C, _stream(w.device)))
+    return out
+
+
 class MoELayer:
     """One MoE FFN layer bound to device weights, with its workspace and
-    output buffer allocated once (calls allocate nothing)."""
+    output buffer allocated once (calls allocate nothing).  Expert weights
+    are given row-major ([E,I,H], [E,I,H], [E,H,I]; shared [Is,H], [Is,H],
+    [H,Is]) and packed once here, unless `packed=True` says they already are."""
 
     def __init__(self, router_w, router_b, w_gate, w_up, w_down, ws_gate=None, ws_up=None,
-                 ws_down=None, K=8, T_max=None, **opts):
+                 ws_down=None, K=8, T_max=None, packed=False, **opts):
         load()
         _dev(router_w, "router_w", torch.float32)
         _dev(router_b, "router_b", torch.float32)
@@ -218,6 +241,11 @@ class MoELayer:
         if self.Is:
             for n, t in (("ws_gate", ws_gate), ("ws_up", ws_up), ("ws_down", ws_down)):
                 _dev(t, n, torch.bfloat16)
+        if not packed:
+            w_gate, w_up, w_down = pack_weights(w_gate), pack_weights(w_up), pack_weights(w_down)
+            if self.Is:
+                ws_gate, ws_up, ws_down = (pack_weights(ws_gate), pack_weights(ws_up),
+                                           pack_weights(ws_down))
         self.tensors = (router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
         self.router = Router(_ptr(router_w), _ptr(router_b))
         self.experts = Experts(_ptr(w_gate), _ptr(w_up), _ptr(w_down))

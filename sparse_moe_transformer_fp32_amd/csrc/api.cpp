@@ -111,14 +111,19 @@ moe_status run_route(const smoe::Plan& p, const moe_opts& o, const uint16_t* x,
                        "route_topk")))
       return st;
   }
+  smoe::RouteLaunch rl{};
+  rl.topk_idx = rbuf.topk_idx;
+  rl.topk_w = rbuf.topk_w;
+  rl.counts = rbuf.counts;
+  rl.offsets = rbuf.offsets;
+  rl.perm = rbuf.perm;
+  rl.slot = rbuf.slot;
+  rl.row_token = reinterpret_cast<int32_t*>(ws + p.ws_row_token);
+  rl.row_w = reinterpret_cast<float*>(ws + p.ws_row_w);
+  rl.rb = reinterpret_cast<smoe::RowBlock*>(ws + p.ws_rb);
+  rl.n_rb = reinterpret_cast<int32_t*>(ws + p.ws_nrb);
   StageMark m(MOE_STAGE_DISPATCH, s);
-  return launched(
-      smoe::launch_dispatch(p, rbuf.topk_idx, rbuf.topk_w, rbuf.counts, rbuf.offsets, rbuf.perm,
-                            rbuf.slot, reinterpret_cast<int32_t*>(ws + p.ws_row_token),
-                            reinterpret_cast<float*>(ws + p.ws_row_w),
-                            reinterpret_cast<smoe::RowBlock*>(ws + p.ws_rb),
-                            reinterpret_cast<int32_t*>(ws + p.ws_nrb), s),
-      "dispatch");
+  return launched(smoe::launch_dispatch(p, rl, s), "dispatch");
 }
 
 RouteBufs bufs_from(const moe_routing* r) {
@@ -343,6 +348,25 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
     StageMark m(MOE_STAGE_COMBINE, stream);
     if ((st = launched(smoe::launch_combine(p, ob, rb.slot, y, stream), "combine"))) return st;
   }
+  return ok();
+}
+
+moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, int32_t rows,
+                            int32_t cols, hipStream_t stream) {
+  if (!src || !dst) return fail(MOE_ERR_NULL, "moe_pack_weights: NULL src or dst");
+  if (n_mats < 1 || rows < 16 || cols < 32 || rows % 16 || cols % 32)
+    return fail(MOE_ERR_SHAPE,
+                "moe_pack_weights: n_mats=%d rows=%d cols=%d (need >= 1, rows %% 16 == 0, "
+                "cols %% 32 == 0)",
+                n_mats, rows, cols);
+  if (misaligned(src) || misaligned(dst))
+    return fail(MOE_ERR_ALIGN, "moe_pack_weights: pointers must be 16-byte aligned");
+  const size_t bytes = (size_t)n_mats * rows * cols * 2;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  if (a < b + bytes && b < a + bytes)
+    return fail(MOE_ERR_OPTION, "moe_pack_weights: src and dst overlap");
+  moe_status st = launched(smoe::launch_pack(src, dst, n_mats, rows, cols, stream), "pack");
+  if (st) return st;
   return ok();
 }
 

@@ -11,7 +11,9 @@
 //
 // Design (weight-streaming): every weight element is read from HBM exactly
 // once per row block and goes straight from global memory into the MFMA A
-// operand registers of the one wave that uses it -- no LDS round trip.  The
+// operand registers of the one wave that uses it -- no LDS round trip.
+// Weights arrive fragment-packed (see pack.hip): each wave-wide A load is one
+// contiguous kilobyte.  The
 // token rows (B operand) are small and hot in L2.  A wave owns FR fragments
 // of 16 weight rows and all 16*NB rows of its row block; KSPLIT waves of a
 // workgroup split K and add their partial sums in a fixed order through LDS
@@ -21,8 +23,8 @@
 // 16x16x32 bf16 MFMA operand layout (lane l, r = l & 15, g = l >> 4):
 //   A: row r, k = 8g..8g+7    B: column r, k = 8g..8g+7
 //   C: rows 4g..4g+3 of column r
-// Any k order shared by A and B gives the same dot product, so each lane
-// reads its 16 contiguous bytes of a weight row and of a token row.
+// Each lane reads its 16 contiguous bytes of a packed weight tile and of a
+// token row at the same k range.
 #include "smoe_internal.h"
 
 namespace smoe {
@@ -80,20 +82,26 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
   const int klen = Kdim / KSPLIT;
   const int kbeg = kp * klen + 8 * g;
 
-  // A operand rows (weights)
+  // A operand: fragment-packed weights (16x32 tiles of 1 KB in lane order,
+  // row-tile-major); this wave walks K inside its row tiles
+  const int ksteps = Kdim / 32;
+  const int kstep0 = kp * (klen / 32);
   const uint16_t* aptr[FR];
   if (MODE == 0) {
     const uint16_t* Wg = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.I * P.H;
     const uint16_t* Wu = shared ? P.sa1 : P.wa1 + (size_t)blk.group * P.I * P.H;
 #pragma unroll
     for (int f = 0; f < FR; ++f) {
-      const int i = cbase + (f >> 1) * 16 + r;
-      aptr[f] = ((f & 1) ? Wu : Wg) + (size_t)i * P.H + kbeg;
+      const int rt = (cbase >> 4) + (f >> 1);
+      aptr[f] = ((f & 1) ? Wu : Wg) + ((size_t)rt * ksteps + kstep0) * 512 + lane * 8;
     }
   } else {
     const uint16_t* Wd = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.H * P.I;
 #pragma unroll
-    for (int f = 0; f < FR; ++f) aptr[f] = Wd + (size_t)(cbase + f * 16 + r) * inter + kbeg;
+    for (int f = 0; f < FR; ++f) {
+      const int rt = (cbase >> 4) + f;
+      aptr[f] = Wd + ((size_t)rt * ksteps + kstep0) * 512 + lane * 8;
+    }
   }
   // B operand rows (tokens); rows past the block repeat its last row
   const uint16_t* bptr[NB];
@@ -125,12 +133,12 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
   auto load = [&](u32x4 (&a)[U][FR], u32x4 (&b)[U][NB], int stage) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k = min(stage * U + u, nsteps - 1) * 32;
+      const int ks = min(stage * U + u, nsteps - 1);
 #pragma unroll
-      for (int f = 0; f < FR; ++f)
-        a[u][f] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(aptr[f] + k));
+      for (int f = 0; f < FR; ++f) a[u][f] = *reinterpret_cast<const u32x4*>(aptr[f] + ks * 512);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + k);
+      for (int nb = 0; nb < NB; ++nb)
+        b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + ks * 32);
     }
   };
   auto compute = [&](const u32x4 (&a)[U][FR], const u32x4 (&b)[U][NB], int stage) {

@@ -25,7 +25,7 @@ namespace smoe {
 // Tile: a workgroup of 4 waves covers 64 experts x (16*NB) tokens; each wave
 // owns 16 experts (the MFMA A operand) and all tokens of the tile (B).  H is
 // split over gridDim.z so that small-T launches still spread the 4.7 MB of
-// router weights over many CUs; each split writes its own partial sums and
+// router weights over many CUs; each split writes its own partial sum and
 // the top-K kernel adds them in a fixed order.
 template <int NB>
 __global__ __launch_bounds__(256) void route_logits_kernel(
@@ -76,8 +76,9 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
     }
   }
   // C layout of the 16x16 MFMA: lane holds rows 4g..4g+3 (experts) of
-  // column r (token).
-  float* out = partial + (size_t)split * T * E;
+  // column r (token).  Partial sums are stored [T][E][S] so that the S
+  // splits of one logit are contiguous for the top-K kernel.
+  const int S = gridDim.z;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int t = t0 + nb * 16 + r;
@@ -85,100 +86,81 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + 4 * g + j;
-      if (e < E) out[(size_t)t * E + e] = acc[nb][j];
+      if (e < E) partial[((size_t)t * E + e) * S + split] = acc[nb][j];
     }
   }
 }
 
 // --------------------------------------------------------------------------
-// Sigmoid, bias, top-K and weights: one wave per token.  Lane l holds the
-// experts l, l+64, l+128, ...  K rounds of a wave-wide argmax (larger key
-// first, equal keys -> lower expert id) pick the set; ballots then list the
-// chosen experts in ascending id.
-__global__ __launch_bounds__(256) void route_topk_kernel(
-    const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E,
-    int K, float scale, int norm, int biw, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w, float* __restrict__ keys_out, float* __restrict__ scores_out) {
+// Top-K and weights for one token, by one wave.  Lane l holds experts
+// l, l+64, l+128, ... (key[c], sc[c] for expert 64c + l).
+//
+// Selection is a radix select, with no cross-lane data movement: keys are
+// mapped to order-preserving unsigned integers, and the K-th largest is found
+// bit by bit from the top (a candidate threshold is kept if at least K keys
+// are >= it; counts come from ballots and scalar popcounts).  The chosen set
+// is every key above that threshold plus, among keys equal to it, the lowest
+// expert ids.  Slots are then listed in ascending expert id, and the weight
+// denominator is summed in that slot order with readlane.
+__device__ inline uint32_t ordered_key(float f) {
+  const uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int C>
+__device__ inline void wave_select(const float (&key)[C], const float (&sc)[C], int E, int K,
+                                   float scale, int norm, int biw, int32_t* idx_out,
+                                   float* w_out) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;
-  const int C = (E + 63) >> 6;
-
-  // logits: sum the split-H partial sums in a fixed order; all loads of a
-  // group of four splits are issued before any add
-  float lg[16];
+  const unsigned long long below = (1ull << lane) - 1ull;
+  uint32_t ok[C];
+  uint32_t valid = 0;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) lg[c] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 4) {
-    float v[16][4];
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int e = min(c * 64 + lane, E - 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        v[c][q] = (c < C && s0 + q < S) ? partial[((size_t)(s0 + q) * T + t) * E + e] : 0.f;
-    }
-#pragma unroll
-    for (int c = 0; c < 16; ++c)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) lg[c] += v[c][q];
+  for (int c = 0; c < C; ++c) {
+    ok[c] = ordered_key(key[c]);
+    if (c * 64 + lane < E) valid |= 1u << c;
   }
-
-  float key[16], sc[16];
+  // K-th largest ordered key (K <= E, so it exists)
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    key[c] = -INFINITY;
-    sc[c] = 0.f;
-    const int e = c * 64 + lane;
-    if (c < C && e < E) {
-      const float l = lg[c];
-      const float sg = 1.0f / (1.0f + expf(-l));
-      const float kk = sg + bias[e];
-      sc[c] = sg;
-      key[c] = kk == kk ? kk : -INFINITY;  // a NaN key never wins (inputs must be finite)
-      if (keys_out) keys_out[(size_t)t * E + e] = kk;
-      if (scores_out) scores_out[(size_t)t * E + e] = sg;
-    }
+    for (int c = 0; c < C; ++c) cnt += __popcll(__ballot(((valid >> c) & 1u) && ok[c] >= cand));
+    if (cnt >= K) thr = cand;
   }
-
+  int n_gt = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) n_gt += __popcll(__ballot(((valid >> c) & 1u) && ok[c] > thr));
+  const int need = K - n_gt;  // >= 1 keys equal to thr, lowest ids first
   uint32_t sel = 0;
-  for (int k = 0; k < K; ++k) {
-    float bk = -INFINITY;
-    int be = 0x7fffffff;
+  int eq_before = 0;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int e = c * 64 + lane;
-      const bool cand = c < C && e < E && !((sel >> c) & 1u);
-      if (cand && (key[c] > bk || (key[c] == bk && e < be))) {
-        bk = key[c];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ok = __shfl_xor(bk, off);
-      const int oe = __shfl_xor(be, off);
-      if (ok > bk || (ok == bk && oe < be)) {
-        bk = ok;
-        be = oe;
-      }
-    }
-    if ((be & 63) == lane) sel |= 1u << (be >> 6);
+  for (int c = 0; c < C; ++c) {
+    const bool v = (valid >> c) & 1u;
+    const bool eq = v && ok[c] == thr;
+    const unsigned long long meq = __ballot(eq);
+    const int rank = eq_before + __popcll(meq & below);
+    if ((v && ok[c] > thr) || (eq && rank < need)) sel |= 1u << c;
+    eq_before += __popcll(meq);
   }
 
-  // weight numerator g = s (bias steers selection only) or s + b
+  // denominator in slot order (ascending expert id)
   float gsum = 0.f;
 #pragma unroll
-  for (int c = 0; c < 16; ++c)
-    if ((sel >> c) & 1u) gsum += biw ? key[c] : sc[c];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) gsum += __shfl_xor(gsum, off);
+  for (int c = 0; c < C; ++c) {
+    unsigned long long m = __ballot((sel >> c) & 1u);
+    const int gbits = __float_as_int(biw ? key[c] : sc[c]);
+    while (m) {
+      const int ln = __builtin_ctzll(m);
+      m &= m - 1ull;
+      gsum += __int_as_float(__builtin_amdgcn_readlane(gbits, ln));
+    }
+  }
 
-  const unsigned long long below = (1ull << lane) - 1ull;
   int base = 0;
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    if (c >= C) break;
+  for (int c = 0; c < C; ++c) {
     const bool mine = (sel >> c) & 1u;
     const unsigned long long m = __ballot(mine);
     if (mine) {
@@ -189,11 +171,74 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
         w = gsum > 0.f ? scale * gv / gsum : scale / (float)K;
       else
         w = scale * gv;
-      topk_idx[(size_t)t * K + j] = c * 64 + lane;
-      topk_w[(size_t)t * K + j] = w;
+      idx_out[j] = c * 64 + lane;
+      w_out[j] = w;
     }
     base += __popcll(m);
   }
+}
+
+// score and key of one expert from its logit; a NaN key never wins (inputs
+// must be finite)
+__device__ inline void score_key(float l, float b, float* sg, float* kk) {
+  *sg = 1.0f / (1.0f + expf(-l));
+  const float k = *sg + b;
+  *kk = k == k ? k : -INFINITY;
+}
+
+// One 64-thread workgroup (one wave) per token: add the S split-H partial
+// logits of each expert (contiguous, loaded as 16-byte vectors, all loads
+// issued before the adds; fixed order), then sigmoid, bias and wave_select.
+// C = ceil(E/64) expert slots per lane, fixed at compile time.
+template <int C>
+__global__ __launch_bounds__(64) void route_topk_kernel(
+    const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E,
+    int K, float scale, int norm, int biw, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w, float* __restrict__ keys_out, float* __restrict__ scores_out) {
+  const int lane = threadIdx.x;
+  const int t = blockIdx.x;
+  const float* prow = partial + (size_t)t * E * S;
+
+  float key[C], sc[C];
+  // four experts' splits in flight at a time keeps the buffer at 128 VGPRs
+#pragma unroll
+  for (int c0 = 0; c0 < C; c0 += 4) {
+    f32x4 v[4][8];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int e = min((c0 + cc) * 64 + lane, E - 1);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (c0 + cc < C && S >= 4 && q < S / 4)
+          v[cc][q] = *reinterpret_cast<const f32x4*>(prow + (size_t)e * S + 4 * q);
+        else if (c0 + cc < C && S < 4 && q == 0)
+          v[cc][q] = f32x4{prow[(size_t)e * S], S > 1 ? prow[(size_t)e * S + 1] : 0.f, 0.f, 0.f};
+        else
+          v[cc][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int c = c0 + cc;
+      if (c < C) {
+        float l = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) l += v[cc][q][j];
+        key[c] = -INFINITY;
+        sc[c] = 0.f;
+        const int e = c * 64 + lane;
+        if (e < E) {
+          score_key(l, bias[e], &sc[c], &key[c]);
+          if (keys_out) keys_out[(size_t)t * E + e] = sc[c] + bias[e];
+          if (scores_out) scores_out[(size_t)t * E + e] = sc[c];
+        }
+      }
+    }
+  }
+  wave_select<C>(key, sc, E, K, scale, norm, biw, topk_idx + (size_t)t * K,
+                 topk_w + (size_t)t * K);
 }
 
 // --------------------------------------------------------------------------
@@ -235,49 +280,60 @@ __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   return ex;
 }
 
-__global__ __launch_bounds__(1024) void dispatch_kernel(
-    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int K,
-    int E, int bn, int has_shared, int rb_max, int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ perm, int32_t* __restrict__ slot_pos,
-    int32_t* __restrict__ row_token, float* __restrict__ row_w, RowBlock* __restrict__ rb,
-    int32_t* __restrict__ n_rb) {
-  __shared__ int s_cnt[1024];
-  __shared__ int s_fill[1024];
-  __shared__ uint32_t s_mask[1024 * 8];
-  __shared__ int s_wave[33];
+struct DispatchArgs {
+  const int32_t* topk_idx;
+  const float* topk_w;
+  int T, K, E, bn, has_shared, rb_max;
+  int32_t *counts, *offsets, *perm, *slot_pos, *row_token;
+  float* row_w;
+  RowBlock* rb;
+  int32_t* n_rb;
+};
+
+// Dynamic LDS: cnt[E], fill[E], mask[8E], wave scratch[36].
+__global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int E = a.E, T = a.T, K = a.K;
+  int* s_cnt = reinterpret_cast<int*>(smem);
+  int* s_fill = s_cnt + E;
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(s_fill + E);
+  int* s_wave = reinterpret_cast<int*>(s_mask + 8 * E);
   const int tid = threadIdx.x;
   const int KT = T * K;
 
+  // expert ids come from the top-K and are in range; the clamp only keeps
+  // LDS indexing in bounds whatever the input
+  auto sel_e = [&](int i) { return min(max(a.topk_idx[i], 0), E - 1); };
+  auto sel_w = [&](int i) { return a.topk_w[i]; };
+
   for (int e = tid; e < E; e += 1024) s_cnt[e] = 0;
   __syncthreads();
-  // expert ids come from route_topk and are in range; the clamp only keeps
-  // LDS indexing in bounds whatever the input
-  for (int i = tid; i < KT; i += 1024) atomicAdd(&s_cnt[min(max(topk_idx[i], 0), E - 1)], 1);
+  for (int i = tid; i < KT; i += 1024) atomicAdd(&s_cnt[sel_e(i)], 1);
   __syncthreads();
 
   // E <= 1024: one expert per thread
   const int cnt = tid < E ? s_cnt[tid] : 0;
   int total;
   const int off = block_exclusive_scan(cnt, s_wave, &total);
-  const int nrb = (cnt + bn - 1) / bn;
+  const int nrb = (cnt + a.bn - 1) / a.bn;
   int rb_total;
   const int rbpos = block_exclusive_scan(nrb, s_wave, &rb_total);
   if (tid < E) {
-    counts[tid] = cnt;
-    offsets[tid] = off;
+    a.counts[tid] = cnt;
+    a.offsets[tid] = off;
     s_fill[tid] = off;
     for (int i = 0; i < nrb; ++i) {
       const int p = rbpos + i;
-      if (p < rb_max) rb[p] = RowBlock{tid, off + i * bn, min(bn, cnt - i * bn), 0};
+      if (p < a.rb_max) a.rb[p] = RowBlock{tid, off + i * a.bn, min(a.bn, cnt - i * a.bn), 0};
     }
   }
-  if (tid == 0) offsets[E] = total;
-  const int nrb_s = has_shared ? (T + bn - 1) / bn : 0;
+  if (tid == 0) a.offsets[E] = total;
+  const int nrb_s = a.has_shared ? (T + a.bn - 1) / a.bn : 0;
   for (int i = tid; i < nrb_s; i += 1024) {
     const int p = rb_total + i;
-    if (p < rb_max) rb[p] = RowBlock{E, KT + i * bn, min(bn, T - i * bn), 0};
+    if (p < a.rb_max) a.rb[p] = RowBlock{E, KT + i * a.bn, min(a.bn, T - i * a.bn), 0};
   }
-  if (tid == 0) n_rb[0] = min(rb_total + nrb_s, rb_max);
+  if (tid == 0) a.n_rb[0] = min(rb_total + nrb_s, a.rb_max);
   __syncthreads();
 
   for (int c0 = 0; c0 < T; c0 += 256) {
@@ -286,7 +342,7 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(
     for (int i = tid; i < 256 * K; i += 1024) {
       const int t = c0 + i / K;
       if (t < T) {
-        const int e = min(max(topk_idx[(size_t)t * K + (i % K)], 0), E - 1);
+        const int e = sel_e(t * K + (i % K));
         const int lt = t - c0;
         atomicOr(&s_mask[e * 8 + (lt >> 5)], 1u << (lt & 31));
       }
@@ -296,16 +352,16 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(
       const int t = c0 + i / K;
       if (t < T) {
         const int j = i % K;
-        const int e = min(max(topk_idx[(size_t)t * K + j], 0), E - 1);
+        const int e = sel_e(t * K + j);
         const int lt = t - c0;
         int rank = 0;
         for (int wd = 0; wd < (lt >> 5); ++wd) rank += __popc(s_mask[e * 8 + wd]);
         rank += __popc(s_mask[e * 8 + (lt >> 5)] & ((1u << (lt & 31)) - 1u));
         const int row = s_fill[e] + rank;
-        perm[row] = t;
-        row_token[row] = t;
-        row_w[row] = topk_w[(size_t)t * K + j];
-        slot_pos[(size_t)t * K + j] = row;
+        a.perm[row] = t;
+        a.row_token[row] = t;
+        a.row_w[row] = sel_w(t * K + j);
+        a.slot_pos[(size_t)t * K + j] = row;
       }
     }
     __syncthreads();
@@ -317,13 +373,15 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(
     }
     __syncthreads();
   }
-  if (has_shared) {
+  if (a.has_shared) {
     for (int t = tid; t < T; t += 1024) {
-      row_token[KT + t] = t;
-      row_w[KT + t] = 1.0f;
+      a.row_token[KT + t] = t;
+      a.row_w[KT + t] = 1.0f;
     }
   }
 }
+
+size_t dispatch_lds_bytes(int E) { return (size_t)E * 4 * 2 + (size_t)E * 8 * 4 + 36 * 4; }
 
 // --------------------------------------------------------------------------
 hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
@@ -342,19 +400,33 @@ hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
 hipError_t launch_route_topk(const Plan& p, const float* partial, const float* bias,
                              float scale, int norm, int biw, int32_t* topk_idx, float* topk_w,
                              float* keys, float* scores, hipStream_t s) {
-  dim3 grid((p.T + 3) / 4);
-  hipLaunchKernelGGL(route_topk_kernel, grid, dim3(256), 0, s, partial, p.route_splits, bias,
-                     p.T, p.E, p.K, scale, norm, biw, topk_idx, topk_w, keys, scores);
+  const int C = (p.E + 63) / 64;
+#define SMOE_TOPK(CC)                                                                          \
+  case CC:                                                                                     \
+    hipLaunchKernelGGL(route_topk_kernel<CC>, dim3(p.T), dim3(64), 0, s, partial,              \
+                       p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx, topk_w, \
+                       keys, scores);                                                          \
+    break;
+  switch (C) {
+    SMOE_TOPK(1) SMOE_TOPK(2) SMOE_TOPK(3) SMOE_TOPK(4) SMOE_TOPK(5) SMOE_TOPK(6)
+    SMOE_TOPK(7) SMOE_TOPK(8) SMOE_TOPK(9) SMOE_TOPK(10) SMOE_TOPK(11) SMOE_TOPK(12)
+    SMOE_TOPK(13) SMOE_TOPK(14) SMOE_TOPK(15) SMOE_TOPK(16)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef SMOE_TOPK
   return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const Plan& p, const int32_t* topk_idx, const float* topk_w,
-                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                           int32_t* slot_pos, int32_t* row_token, float* row_w, RowBlock* rb,
-                           int32_t* n_rb, hipStream_t s) {
-  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(1024), 0, s, topk_idx, topk_w, p.T, p.K,
-                     p.E, p.bn, p.Is > 0 ? 1 : 0, p.rb_max, counts, offsets, perm_token,
-                     slot_pos, row_token, row_w, rb, n_rb);
+hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
+  DispatchArgs a{};
+  a.topk_idx = r.topk_idx;
+  a.topk_w = r.topk_w;
+  a.T = p.T; a.K = p.K; a.E = p.E; a.bn = p.bn; a.has_shared = p.Is > 0 ? 1 : 0;
+  a.rb_max = p.rb_max;
+  a.counts = r.counts; a.offsets = r.offsets; a.perm = r.perm; a.slot_pos = r.slot;
+  a.row_token = r.row_token; a.row_w = r.row_w; a.rb = r.rb; a.n_rb = r.n_rb;
+  hipLaunchKernelGGL(dispatch_kernel, dim3(1), dim3(1024), dispatch_lds_bytes(p.E), s, a);
   return hipGetLastError();
 }
 

@@ -55,10 +55,17 @@ hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
 hipError_t launch_route_topk(const Plan& p, const float* partial, const float* bias,
                              float scale, int norm, int bias_in_weights, int32_t* topk_idx,
                              float* topk_w, float* keys, float* scores, hipStream_t s);
-hipError_t launch_dispatch(const Plan& p, const int32_t* topk_idx, const float* topk_w,
-                           int32_t* counts, int32_t* offsets, int32_t* perm_token,
-                           int32_t* slot_pos, int32_t* row_token, float* row_w,
-                           RowBlock* rb, int32_t* n_rb, hipStream_t s);
+// Everything the dispatch launch touches: it reads topk_idx/topk_w.
+struct RouteLaunch {
+  const int32_t* topk_idx;
+  const float* topk_w;
+  int32_t *counts, *offsets, *perm, *slot, *row_token;
+  float* row_w;
+  RowBlock* rb;
+  int32_t* n_rb;
+};
+size_t dispatch_lds_bytes(int E);
+hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s);
 
 struct GateUpArgs {
   const uint16_t* wg;   // [E, I, H]
@@ -83,6 +90,9 @@ struct DownArgs {
 };
 hipError_t launch_gate_up(const Plan& p, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down(const Plan& p, const DownArgs& a, hipStream_t s);
+
+hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,
+                       hipStream_t s);
 
 hipError_t launch_combine(const Plan& p, const uint16_t* o, const int32_t* slot_pos,
                           uint16_t* y, hipStream_t s);

@@ -171,3 +171,14 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros((16, 4096), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         B.route(x, torch.zeros((288, 4096)), torch.zeros(288), 8)
+
+
+def test_pack_weights_checks():
+    lib = B.load()
+    f = lib.moe_pack_weights
+    assert f(None, _vp(A), 1, 16, 32, None) == B.MOE_ERR_NULL
+    assert f(_vp(A), _vp(1 << 30), 1, 8, 32, None) == B.MOE_ERR_SHAPE
+    assert f(_vp(A), _vp(1 << 30), 1, 16, 48, None) == B.MOE_ERR_SHAPE
+    assert f(_vp(A), _vp(1 << 30), 0, 16, 32, None) == B.MOE_ERR_SHAPE
+    assert f(_vp(A + 2), _vp(1 << 30), 1, 16, 32, None) == B.MOE_ERR_ALIGN
+    assert f(_vp(A), _vp(A + 512), 1, 16, 32, None) == B.MOE_ERR_OPTION   # overlap

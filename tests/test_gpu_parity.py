@@ -230,3 +230,20 @@ def test_chain_teacher_forced_small():
         torch.cuda.synchronize()
         check_output(host_f64(r_new), host_f64(r) + y, f"residual {li}")
         r = r_new
+
+
+# ---------------------------------------------------------------- packing
+def test_pack_layout_bit_exact():
+    """moe_pack_weights against the layout formula in the header."""
+    n, R, C = 3, 48, 96
+    w = torch.randn(n, R, C, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    got = B.pack_weights(w.to(DEV)).cpu().view(torch.int16).numpy().reshape(-1)
+    src = w.view(torch.int16).numpy()
+    want = np.empty(n * R * C, np.int16)
+    for m in range(n):
+        for row in range(R):
+            for col in range(C):
+                rt, kt, r, c = row // 16, col // 32, row % 16, col % 32
+                off = m * R * C + (rt * (C // 32) + kt) * 512 + 8 * (16 * (c // 8) + r) + c % 8
+                want[off] = src[m, row, col]
+    assert np.array_equal(got, want)
