@@ -244,6 +244,9 @@ def main():
                     choices=["decode", "prefill", "skew", "skew_mild", "long", "tiny"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 side measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the "
+                         "known-size reference for HBM byte counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; --gpus must be 1.",
@@ -252,6 +255,14 @@ def main():
 
     import torch
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}))
+        return
     res = run_layer_bench(args.workload, args.steps, args.warmup)
     wl = res["wl"]
     work = layer_work(wl, res["counts"])

@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsmoe_gfx950.so")
 
-SOURCES = ["route.hip", "expert_gemm.hip", "combine.hip", "pack.hip", "api.cpp"]
+SOURCES = ["route.hip", "expert_gemm.hip", "expert_gemm_lds.hip", "combine.hip", "pack.hip",
+           "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

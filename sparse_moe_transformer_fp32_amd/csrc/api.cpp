@@ -177,8 +177,8 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
 
   // grouped GEMMs: row-block height follows the mean rows per expert
   const double avg = (double)K * T / E;
-  int nb = avg <= 16 ? 1 : avg <= 32 ? 2 : avg <= 64 ? 4 : 8;
-  if (nb == 8 && !(I % 128 == 0 && Is % 128 == 0 && H % 256 == 0)) nb = 4;
+  int nb = avg <= 16 ? 1 : avg <= 32 ? 2 : avg <= 64 ? 4 : 12;
+  if (nb == 12 && !(I % 128 == 0 && Is % 128 == 0 && H % 256 == 0)) nb = 4;
   p->nb = nb;
   p->bn = 16 * nb;
   p->rb_max = std::min(E, p->KT) + p->KT / p->bn + (Is > 0 ? (T + p->bn - 1) / p->bn : 0);
@@ -191,7 +191,7 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
     p->ksplit_gu = p->ksplit_dn = 1;
     p->gu_rows_wg = 64;
     p->dn_rows_wg = 128;
-  } else {
+  } else {  // LDS-pipelined kernels: 128 gate/up columns or 256 down rows
     p->ksplit_gu = p->ksplit_dn = 1;
     p->gu_rows_wg = 128;
     p->dn_rows_wg = 256;
@@ -329,7 +329,9 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
   ga.limit_shared = o.swiglu_limit_shared;
   {
     StageMark m(MOE_STAGE_GATE_UP, stream);
-    if ((st = launched(smoe::launch_gate_up(p, ga, stream), "gate_up"))) return st;
+    const hipError_t e =
+        p.nb == 12 ? smoe::launch_gate_up_lds(p, ga, stream) : smoe::launch_gate_up(p, ga, stream);
+    if ((st = launched(e, "gate_up"))) return st;
   }
 
   smoe::DownArgs da{};
@@ -342,7 +344,9 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
   da.o = ob;
   {
     StageMark m(MOE_STAGE_DOWN, stream);
-    if ((st = launched(smoe::launch_down(p, da, stream), "down"))) return st;
+    const hipError_t e =
+        p.nb == 12 ? smoe::launch_down_lds(p, da, stream) : smoe::launch_down(p, da, stream);
+    if ((st = launched(e, "down"))) return st;
   }
   {
     StageMark m(MOE_STAGE_COMBINE, stream);

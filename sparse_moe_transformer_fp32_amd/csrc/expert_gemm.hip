@@ -233,11 +233,11 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
 }
 
 // --------------------------------------------------------------------------
-// Launch configurations.  Small row blocks (decode): one 16-row fragment pair
-// per wave, four waves split K, so a workgroup streams 16 x 2 x H weights and
-// there are many small workgroups to balance.  Large row blocks (prefill):
-// 8 token blocks (128 rows) per wave and two fragment pairs, waves own
-// different weight rows.
+// Launch configurations.  Row blocks of 16 tokens (decode): one 16-row
+// fragment pair per wave, four waves split K, so a workgroup streams
+// 16 x 2 x H weights and there are many small workgroups to balance.  Row
+// blocks of 32 or 64 tokens: waves own different weight rows.  Larger row
+// blocks use the LDS-pipelined kernels (expert_gemm_lds.hip).
 template <int MODE>
 static hipError_t launch_mode(const Plan& p, const GemmParams& gp, int ksplit, hipStream_t s) {
   const int grid = p.rb_max * gp.tiles;
@@ -258,8 +258,7 @@ static hipError_t launch_mode(const Plan& p, const GemmParams& gp, int ksplit, h
       hipLaunchKernelGGL((expert_gemm_kernel<MODE, 4, 2, 1, 2>), dim3(grid), dim3(256), 0, s, gp);
       break;
     default:
-      hipLaunchKernelGGL((expert_gemm_kernel<MODE, 8, 4, 1, 1>), dim3(grid), dim3(256), 0, s, gp);
-      break;
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -32,7 +32,7 @@ struct Plan {
   int32_t rows_total;    // KT + (Is > 0 ? T : 0)
   int32_t route_tok;     // tokens per router tile (16 or 64)
   int32_t route_splits;  // split of H across router workgroups
-  int32_t nb;            // 16-token column blocks per GEMM tile
+  int32_t nb;            // 16-token column blocks per GEMM tile (1, 2, 4; 12 = LDS kernels)
   int32_t bn;            // rows per row block = 16 * nb
   int32_t rb_max;        // upper bound on row blocks
   int32_t ksplit_gu;     // waves splitting K in the gate/up GEMM
@@ -90,6 +90,9 @@ struct DownArgs {
 };
 hipError_t launch_gate_up(const Plan& p, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down(const Plan& p, const DownArgs& a, hipStream_t s);
+// large row blocks (plan nb == 12): LDS-pipelined variants
+hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,
                        hipStream_t s);

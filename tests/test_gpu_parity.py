@@ -1,7 +1,8 @@
 """HIP path vs CPU oracle, element by element, through the C-ABI (gfx950 GPU).
 
-Small cases cover every tiling variant (row-block heights 16/32/64/128,
-split-K 1/2/4), ragged tails, T=1, K=1, K=E, E not a multiple of 64, the
+Small cases cover every tiling variant (row blocks of 16/32/64 tokens with
+split-K 1/2/4 in the register-streaming kernels, 192-token blocks in the
+LDS-pipelined kernels, and the fallback when shapes exclude them), ragged tails, T=1, K=1, K=E, E not a multiple of 64, the
 largest E and K, no shared expert, the SwiGLU clamp and the alternative bias
 reading.  Flash-shaped cases run the same launch configuration as the
 benchmark: full outputs at T=16 and sampled rows at T=4096/8192.
@@ -74,8 +75,9 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "ragged_nb1_ksplit2": (101, 37, 384, 40, 6, 192, 128),
     "nb2": (102, 100, 256, 8, 2, 128, 64),
     "nb4": (103, 200, 256, 8, 2, 128, 128),
-    "nb8": (104, 300, 256, 8, 2, 128, 128),
-    "nb8_fallback_nb4": (105, 300, 384, 8, 2, 192, 64),
+    "lds_block": (104, 300, 256, 8, 2, 128, 128),
+    "lds_fallback_nb4": (105, 300, 384, 8, 2, 192, 64),
+    "lds_I_ne_Is": (114, 400, 256, 8, 2, 128, 256),
     "no_shared": (106, 50, 256, 16, 4, 64, 0),
     "T1": (107, 1, 256, 16, 4, 64, 64),
     "K1": (108, 40, 256, 16, 1, 64, 64),
@@ -83,7 +85,7 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "E100": (110, 33, 256, 100, 8, 64, 64),
     "E1024_K16": (111, 20, 256, 1024, 16, 64, 64),
     "I_ne_Is": (112, 70, 256, 12, 3, 128, 192),
-    "long_ragged_nb8": (113, 1000, 256, 6, 2, 128, 128),
+    "lds_multi_block": (113, 1000, 256, 6, 2, 128, 128),
 }
 
 
