@@ -122,6 +122,9 @@ moe_status run_route(const smoe::Plan& p, const moe_opts& o, const uint16_t* x,
   rl.row_w = reinterpret_cast<float*>(ws + p.ws_row_w);
   rl.rb = reinterpret_cast<smoe::RowBlock*>(ws + p.ws_rb);
   rl.n_rb = reinterpret_cast<int32_t*>(ws + p.ws_nrb);
+  rl.lrank = reinterpret_cast<int32_t*>(ws + p.ws_lrank);
+  rl.hist = reinterpret_cast<int32_t*>(ws + p.ws_hist);
+  rl.block_base = reinterpret_cast<int32_t*>(ws + p.ws_bbase);
   StageMark m(MOE_STAGE_DISPATCH, s);
   return launched(smoe::launch_dispatch(p, rl, s), "dispatch");
 }
@@ -168,12 +171,18 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
   p->rows_total = p->KT + (Is > 0 ? T : 0);
 
   // router: 16-token tiles for decode, 64 otherwise; split H until the
-  // launch has ~256 workgroups (each split keeps >= 128 columns)
+  // launch has ~1024 workgroups (each split keeps >= 256 columns) so that
+  // loads of many waves overlap
   p->route_tok = T <= 16 ? 16 : 64;
   const int tiles = ((T + p->route_tok - 1) / p->route_tok) * ((E + 63) / 64);
   int S = 1;
-  while (S < 32 && tiles * S < 256 && H % (2 * S * 128) == 0) S *= 2;
+  const int min_cols = T <= 64 ? 128 : 256;
+  while (S < 32 && tiles * S < 1024 && H % (2 * S * min_cols) == 0) S *= 2;
   p->route_splits = S;
+
+  // dispatch: one workgroup for small T, three kernels over 256-token blocks
+  // for large T
+  p->dispatch_blocks = T > 1024 ? (T + 255) / 256 : 0;
 
   // grouped GEMMs: row-block height follows the mean rows per expert
   const double avg = (double)K * T / E;
@@ -217,6 +226,10 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
   p->ws_row_w = take((size_t)p->rows_total * 4);
   p->ws_rb = take((size_t)p->rb_max * sizeof(RowBlock));
   p->ws_nrb = take(16);
+  const size_t nblk = (size_t)p->dispatch_blocks;
+  p->ws_lrank = take(nblk ? KT * 4 : 0);
+  p->ws_hist = take(nblk * E * 4);
+  p->ws_bbase = take(nblk * E * 4);
   p->ws_h = take((KT * I + (size_t)T * Is) * 2);
   p->ws_o = take((size_t)p->rows_total * H * 2);
   p->ws_total = off;

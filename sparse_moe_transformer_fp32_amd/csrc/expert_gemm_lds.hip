@@ -278,7 +278,7 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
   gp.row_token = a.row_token; gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.h;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.gu_tiles;
   gp.limit = a.limit; gp.limit_shared = a.limit_shared;
-  hipLaunchKernelGGL((expert_gemm_lds_kernel<0, 12, 5>), dim3(lds_grid(p, p.gu_tiles)), dim3(256),
+  hipLaunchKernelGGL((expert_gemm_lds_kernel<0, 12, 4>), dim3(lds_grid(p, p.gu_tiles)), dim3(256),
                      0, s, gp);
   return hipGetLastError();
 }
@@ -288,7 +288,7 @@ hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
   gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.o;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.dn_tiles;
-  hipLaunchKernelGGL((expert_gemm_lds_kernel<1, 12, 5>), dim3(lds_grid(p, p.dn_tiles)), dim3(256),
+  hipLaunchKernelGGL((expert_gemm_lds_kernel<1, 12, 4>), dim3(lds_grid(p, p.dn_tiles)), dim3(256),
                      0, s, gp);
   return hipGetLastError();
 }

@@ -27,7 +27,7 @@ namespace smoe {
 // split over gridDim.z so that small-T launches still spread the 4.7 MB of
 // router weights over many CUs; each split writes its own partial sum and
 // the top-K kernel adds them in a fixed order.
-template <int NB>
+template <int NB, int U>
 __global__ __launch_bounds__(256) void route_logits_kernel(
     const uint16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
     int T, int H, int E, int klen) {
@@ -50,31 +50,64 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-#pragma unroll 2
-  for (int k = 0; k < klen; k += 32) {
-    const f32x4 w0 = *reinterpret_cast<const f32x4*>(wrow + k);
-    const f32x4 w1 = *reinterpret_cast<const f32x4*>(wrow + k + 4);
-    bf16x8 hi, mid, lo;
+  // two register stages of U k-steps; every load is unconditional (steps
+  // past the end re-read the last chunk and skip their MFMAs)
+  const int nsteps = klen / 32;
+  const int nstages = (nsteps + U - 1) / U;
+  f32x4 wa[U][2], wb[U][2];
+  u32x4 xa[U][NB], xb[U][NB];
+  auto load = [&](f32x4 (&w)[U][2], u32x4 (&xv)[U][NB], int stage) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float w = j < 4 ? w0[j] : w1[j - 4];
-      const __bf16 h = (__bf16)w;
-      const float r1 = w - (float)h;
-      const __bf16 m = (__bf16)r1;
-      const float r2 = r1 - (float)m;
-      hi[j] = h;
-      mid[j] = m;
-      lo[j] = (__bf16)r2;
-    }
+    for (int u = 0; u < U; ++u) {
+      const int k = min(stage * U + u, nsteps - 1) * 32;
+      w[u][0] = *reinterpret_cast<const f32x4*>(wrow + k);
+      w[u][1] = *reinterpret_cast<const f32x4*>(wrow + k + 4);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(xrow[nb] + k);
-      const bf16x8 b = __builtin_bit_cast(bf16x8, xv);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[nb], 0, 0, 0);
-      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) xv[u][nb] = *reinterpret_cast<const u32x4*>(xrow[nb] + k);
     }
+  };
+  auto compute = [&](const f32x4 (&w)[U][2], const u32x4 (&xv)[U][NB], int stage) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (stage * U + u < nsteps) {
+        bf16x8 hi, mid, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float wv = j < 4 ? w[u][0][j] : w[u][1][j - 4];
+          const __bf16 h = (__bf16)wv;
+          const float r1 = wv - (float)h;
+          const __bf16 m = (__bf16)r1;
+          const float r2 = r1 - (float)m;
+          hi[j] = h;
+          mid[j] = m;
+          lo[j] = (__bf16)r2;
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 b = __builtin_bit_cast(bf16x8, xv[u][nb]);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[nb], 0, 0, 0);
+          acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[nb], 0, 0, 0);
+        }
+      }
+    }
+  };
+  load(wa, xa, 0);
+  int st = 0;
+  for (; st + 2 < nstages; st += 2) {
+    load(wb, xb, st + 1);
+    compute(wa, xa, st);
+    load(wa, xa, st + 2);
+    compute(wb, xb, st + 1);
   }
+  if (st + 1 < nstages) {
+    load(wb, xb, st + 1);
+    compute(wa, xa, st);
+    compute(wb, xb, st + 1);
+  } else {
+    compute(wa, xa, st);
+  }
+
   // C layout of the 16x16 MFMA: lane holds rows 4g..4g+3 (experts) of
   // column r (token).  Partial sums are stored [T][E][S] so that the S
   // splits of one logit are contiguous for the top-K kernel.
@@ -280,6 +313,37 @@ __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   return ex;
 }
 
+// counts, offsets (exclusive scan) and the GEMM row-block list from one
+// expert count per thread of a 1024-thread workgroup; returns this thread's
+// offset.  Every thread must call it.
+__device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int has_shared,
+                                    int rb_max, int* s_wave, int32_t* counts, int32_t* offsets,
+                                    RowBlock* rb, int32_t* n_rb) {
+  const int tid = threadIdx.x;
+  const int KT = T * K;
+  int total;
+  const int off = block_exclusive_scan(cnt, s_wave, &total);
+  const int nrb = (cnt + bn - 1) / bn;
+  int rb_total;
+  const int rbpos = block_exclusive_scan(nrb, s_wave, &rb_total);
+  if (tid < E) {
+    counts[tid] = cnt;
+    offsets[tid] = off;
+    for (int i = 0; i < nrb; ++i) {
+      const int p = rbpos + i;
+      if (p < rb_max) rb[p] = RowBlock{tid, off + i * bn, min(bn, cnt - i * bn), 0};
+    }
+  }
+  if (tid == 0) offsets[E] = total;
+  const int nrb_s = has_shared ? (T + bn - 1) / bn : 0;
+  for (int i = tid; i < nrb_s; i += blockDim.x) {
+    const int p = rb_total + i;
+    if (p < rb_max) rb[p] = RowBlock{E, KT + i * bn, min(bn, T - i * bn), 0};
+  }
+  if (tid == 0) n_rb[0] = min(rb_total + nrb_s, rb_max);
+  return off;
+}
+
 struct DispatchArgs {
   const int32_t* topk_idx;
   const float* topk_w;
@@ -313,27 +377,9 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 
   // E <= 1024: one expert per thread
   const int cnt = tid < E ? s_cnt[tid] : 0;
-  int total;
-  const int off = block_exclusive_scan(cnt, s_wave, &total);
-  const int nrb = (cnt + a.bn - 1) / a.bn;
-  int rb_total;
-  const int rbpos = block_exclusive_scan(nrb, s_wave, &rb_total);
-  if (tid < E) {
-    a.counts[tid] = cnt;
-    a.offsets[tid] = off;
-    s_fill[tid] = off;
-    for (int i = 0; i < nrb; ++i) {
-      const int p = rbpos + i;
-      if (p < a.rb_max) a.rb[p] = RowBlock{tid, off + i * a.bn, min(a.bn, cnt - i * a.bn), 0};
-    }
-  }
-  if (tid == 0) a.offsets[E] = total;
-  const int nrb_s = a.has_shared ? (T + a.bn - 1) / a.bn : 0;
-  for (int i = tid; i < nrb_s; i += 1024) {
-    const int p = rb_total + i;
-    if (p < a.rb_max) a.rb[p] = RowBlock{E, KT + i * a.bn, min(a.bn, T - i * a.bn), 0};
-  }
-  if (tid == 0) a.n_rb[0] = min(rb_total + nrb_s, a.rb_max);
+  const int off = finish_counts(cnt, E, T, K, a.bn, a.has_shared, a.rb_max, s_wave, a.counts,
+                                a.offsets, a.rb, a.n_rb);
+  if (tid < E) s_fill[tid] = off;
   __syncthreads();
 
   for (int c0 = 0; c0 < T; c0 += 256) {
@@ -384,16 +430,111 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 size_t dispatch_lds_bytes(int E) { return (size_t)E * 4 * 2 + (size_t)E * 8 * 4 + 36 * 4; }
 
 // --------------------------------------------------------------------------
+// Dispatch for large T in three steps, so that many CUs share the work.
+// Block b holds tokens [256b, 256b + 256).
+//  1. local: per block, the 256-bit LDS mask of each expert gives every
+//     selection its rank among the block's earlier tokens for that expert,
+//     and the block's per-expert histogram.
+//  2. scan (one workgroup): per expert, the number of rows of all earlier
+//     blocks; then counts, offsets and the row-block list.
+//  3. scatter: row = offsets[e] + earlier blocks' rows + local rank.
+__global__ __launch_bounds__(256) void dispatch_local_kernel(const int32_t* __restrict__ topk_idx,
+                                                             int T, int K, int E,
+                                                             int32_t* __restrict__ lrank,
+                                                             int32_t* __restrict__ hist) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  uint32_t* s_mask = reinterpret_cast<uint32_t*>(smem);  // 8E words
+  const int tid = threadIdx.x, blk = blockIdx.x;
+  const int t0 = blk * 256;
+  for (int i = tid; i < E * 8; i += 256) s_mask[i] = 0u;
+  __syncthreads();
+  for (int i = tid; i < 256 * K; i += 256) {
+    const int t = t0 + i / K;
+    if (t < T) {
+      const int e = min(max(topk_idx[(size_t)t * K + (i % K)], 0), E - 1);
+      const int lt = t - t0;
+      atomicOr(&s_mask[e * 8 + (lt >> 5)], 1u << (lt & 31));
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 256 * K; i += 256) {
+    const int t = t0 + i / K;
+    if (t < T) {
+      const int j = i % K;
+      const int e = min(max(topk_idx[(size_t)t * K + j], 0), E - 1);
+      const int lt = t - t0;
+      int rank = 0;
+      for (int wd = 0; wd < (lt >> 5); ++wd) rank += __popc(s_mask[e * 8 + wd]);
+      rank += __popc(s_mask[e * 8 + (lt >> 5)] & ((1u << (lt & 31)) - 1u));
+      lrank[(size_t)t * K + j] = rank;
+    }
+  }
+  for (int e = tid; e < E; e += 256) {
+    int n = 0;
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) n += __popc(s_mask[e * 8 + wd]);
+    hist[(size_t)blk * E + e] = n;
+  }
+}
+
+__global__ __launch_bounds__(1024) void dispatch_scan_kernel(
+    const int32_t* __restrict__ hist, int nblk, int T, int K, int E, int bn, int has_shared,
+    int rb_max, int32_t* __restrict__ block_base, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, RowBlock* __restrict__ rb, int32_t* __restrict__ n_rb) {
+  __shared__ int s_wave[36];
+  const int tid = threadIdx.x;
+  int cnt = 0;
+  if (tid < E) {
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) v[q] = b0 + q < nblk ? hist[(size_t)(b0 + q) * E + tid] : 0;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        if (b0 + q < nblk) {
+          block_base[(size_t)(b0 + q) * E + tid] = cnt;
+          cnt += v[q];
+        }
+      }
+    }
+  }
+  finish_counts(cnt, E, T, K, bn, has_shared, rb_max, s_wave, counts, offsets, rb, n_rb);
+}
+
+__global__ __launch_bounds__(256) void dispatch_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, const float* __restrict__ topk_w,
+    const int32_t* __restrict__ lrank, const int32_t* __restrict__ block_base,
+    const int32_t* __restrict__ offsets, int T, int K, int E, int has_shared,
+    int32_t* __restrict__ perm, int32_t* __restrict__ slot_pos, int32_t* __restrict__ row_token,
+    float* __restrict__ row_w) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int KT = T * K;
+  if (i < KT) {
+    const int t = i / K;
+    const int e = min(max(topk_idx[i], 0), E - 1);
+    const int row = offsets[e] + block_base[(size_t)(t >> 8) * E + e] + lrank[i];
+    perm[row] = t;
+    row_token[row] = t;
+    row_w[row] = topk_w[i];
+    slot_pos[i] = row;
+  }
+  if (has_shared && i < T) {
+    row_token[KT + i] = i;
+    row_w[KT + i] = 1.0f;
+  }
+}
+
+// --------------------------------------------------------------------------
 hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
                                float* partial, hipStream_t s) {
   const int klen = p.H / p.route_splits;
   dim3 grid((p.T + p.route_tok - 1) / p.route_tok, (p.E + 63) / 64, p.route_splits);
   if (p.route_tok == 16)
-    hipLaunchKernelGGL(route_logits_kernel<1>, grid, dim3(256), 0, s, x, W, partial, p.T, p.H,
-                       p.E, klen);
+    hipLaunchKernelGGL((route_logits_kernel<1, 4>), grid, dim3(256), 0, s, x, W, partial, p.T,
+                       p.H, p.E, klen);
   else
-    hipLaunchKernelGGL(route_logits_kernel<4>, grid, dim3(256), 0, s, x, W, partial, p.T, p.H,
-                       p.E, klen);
+    hipLaunchKernelGGL((route_logits_kernel<4, 2>), grid, dim3(256), 0, s, x, W, partial, p.T,
+                       p.H, p.E, klen);
   return hipGetLastError();
 }
 
@@ -419,10 +560,23 @@ hipError_t launch_route_topk(const Plan& p, const float* partial, const float* b
 }
 
 hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
+  const int has_shared = p.Is > 0 ? 1 : 0;
+  if (p.dispatch_blocks > 0) {
+    const int nblk = p.dispatch_blocks;
+    hipLaunchKernelGGL(dispatch_local_kernel, dim3(nblk), dim3(256), (size_t)p.E * 8 * 4, s,
+                       r.topk_idx, p.T, p.K, p.E, r.lrank, r.hist);
+    hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, r.hist, nblk, p.T, p.K,
+                       p.E, p.bn, has_shared, p.rb_max, r.block_base, r.counts, r.offsets, r.rb,
+                       r.n_rb);
+    hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((p.KT + 255) / 256), dim3(256), 0, s,
+                       r.topk_idx, r.topk_w, r.lrank, r.block_base, r.offsets, p.T, p.K, p.E,
+                       has_shared, r.perm, r.slot, r.row_token, r.row_w);
+    return hipGetLastError();
+  }
   DispatchArgs a{};
   a.topk_idx = r.topk_idx;
   a.topk_w = r.topk_w;
-  a.T = p.T; a.K = p.K; a.E = p.E; a.bn = p.bn; a.has_shared = p.Is > 0 ? 1 : 0;
+  a.T = p.T; a.K = p.K; a.E = p.E; a.bn = p.bn; a.has_shared = has_shared;
   a.rb_max = p.rb_max;
   a.counts = r.counts; a.offsets = r.offsets; a.perm = r.perm; a.slot_pos = r.slot;
   a.row_token = r.row_token; a.row_w = r.row_w; a.rb = r.rb; a.n_rb = r.n_rb;

@@ -32,6 +32,7 @@ struct Plan {
   int32_t rows_total;    // KT + (Is > 0 ? T : 0)
   int32_t route_tok;     // tokens per router tile (16 or 64)
   int32_t route_splits;  // split of H across router workgroups
+  int32_t dispatch_blocks;  // > 0: three-kernel dispatch over this many 256-token blocks
   int32_t nb;            // 16-token column blocks per GEMM tile (1, 2, 4; 12 = LDS kernels)
   int32_t bn;            // rows per row block = 16 * nb
   int32_t rb_max;        // upper bound on row blocks
@@ -43,7 +44,8 @@ struct Plan {
   int32_t dn_tiles;      // workgroups per row block (down)
   // workspace byte offsets
   size_t ws_partial, ws_topk_idx, ws_topk_w, ws_counts, ws_offsets, ws_perm,
-      ws_slot, ws_row_token, ws_row_w, ws_rb, ws_nrb, ws_h, ws_o, ws_total;
+      ws_slot, ws_row_token, ws_row_w, ws_rb, ws_nrb, ws_lrank, ws_hist, ws_bbase, ws_h, ws_o,
+      ws_total;
 };
 
 void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p);
@@ -63,6 +65,7 @@ struct RouteLaunch {
   float* row_w;
   RowBlock* rb;
   int32_t* n_rb;
+  int32_t *lrank, *hist, *block_base;   // three-kernel dispatch scratch
 };
 size_t dispatch_lds_bytes(int E);
 hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s);

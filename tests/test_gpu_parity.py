@@ -86,6 +86,8 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "E1024_K16": (111, 20, 256, 1024, 16, 64, 64),
     "I_ne_Is": (112, 70, 256, 12, 3, 128, 192),
     "lds_multi_block": (113, 1000, 256, 6, 2, 128, 128),
+    "dispatch_blocks_ragged": (115, 1500, 256, 16, 4, 128, 64),
+    "dispatch_blocks_E1024": (116, 1300, 256, 1024, 16, 64, 64),
 }
 
 
