@@ -138,21 +138,13 @@ def run_layer_bench(wl_name, steps, warmup, device="cuda"):
     routing = B.alloc_routing(T, wl.E, wl.K, device)
     nl = len(layers)
     y = torch.empty_like(x)
-    r_buf = [torch.empty_like(x) for _ in range(2)]
-    xn = torch.empty_like(x)
+    chain = B.MoEChain(layers, eps=1e-6) if nl > 1 else None
 
     def step():
-        if nl == 1:
+        if chain is None:
             layers[0].forward(x, y, routing)
-            return
-        # pre-norm residual stream through chained layers
-        r = x
-        for li, lay in enumerate(layers):
-            B.residual_rmsnorm(r, None, None, 1e-6, None, xn, want_r=False)
-            lay.forward(xn, y, routing if li == nl - 1 else None)
-            r_next = r_buf[li % 2]
-            B.residual_rmsnorm(r, y, None, 1e-6, r_next, None, want_x=False)
-            r = r_next
+        else:  # pre-norm residual stream through the chained layers
+            chain.forward(x, routing_last=routing)
 
     for _ in range(warmup):
         step()

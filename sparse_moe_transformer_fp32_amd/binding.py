@@ -327,3 +327,47 @@ def residual_rmsnorm(r_in: torch.Tensor, y_add: Optional[torch.Tensor] = None,
     _check(lib.moe_residual_rmsnorm(T, H, _ptr(r_in), _ptr(y_add), _ptr(gamma), float(eps),
                                     _ptr(r_out), _ptr(x_out), _stream(r_in.device)))
     return r_out, x_out
+
+
+class MoEChain:
+    """Pre-norm residual stream through chained MoE layers:
+        x_0 = RMSNorm(r_0);  r_{l+1} = r_l + MoE_l(x_l);  x_{l+1} = RMSNorm(r_{l+1})
+    with one moe_residual_rmsnorm call at each layer boundary (residual add
+    and the next layer's norm together).  Returns the last residual stream.
+    Buffers are allocated once per batch size."""
+
+    def __init__(self, layers, eps: float = 1e-6, gamma: Optional[torch.Tensor] = None):
+        self.layers = list(layers)
+        self.eps = float(eps)
+        self.gamma = gamma
+        self._bufs = None
+
+    def _buffers(self, x):
+        if self._bufs is None or self._bufs[0].shape != x.shape:
+            self._bufs = tuple(torch.empty_like(x) for _ in range(4))
+        return self._bufs
+
+    def forward(self, r0: torch.Tensor, capture: bool = False,
+                routing_last: Optional[Dict[str, torch.Tensor]] = None):
+        """capture=True also returns, per layer, (r_l, x_l, y_l, routing_l)
+        copies (routing with keys and scores) for checking.  routing_last
+        receives the last layer's routing."""
+        xn, y, ra, rb = self._buffers(r0)
+        trace = []
+        residual_rmsnorm(r0, None, self.gamma, self.eps, None, xn, want_r=False)
+        r = r0
+        for li, lay in enumerate(self.layers):
+            rt = alloc_routing(r0.shape[0], lay.E, lay.K, r0.device, keys=True) if capture else None
+            if rt is None and li == len(self.layers) - 1:
+                rt = routing_last
+            lay.forward(xn, y, rt)
+            if capture:
+                trace.append((r.clone(), xn.clone(), y.clone(), rt))
+            r_next = ra if li % 2 == 0 else rb
+            last = li == len(self.layers) - 1
+            residual_rmsnorm(r, y, self.gamma, self.eps, r_next, None if last else xn,
+                             want_x=not last)
+            r = r_next
+        return (r, trace) if capture else r
+
+    __call__ = forward

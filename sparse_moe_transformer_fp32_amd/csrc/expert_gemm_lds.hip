@@ -14,21 +14,30 @@
 // every token fragment of the block, so each weight element is read from
 // HBM once per row block.
 //
-// Pipeline: a ring of NS stages in LDS, one 32-wide k-step per stage.  Every
-// operand tile is moved global -> LDS by global_load_lds_dwordx4 (lane l's
-// 16 bytes land at tile base + 16 l): a packed weight tile is one contiguous
-// kilobyte already in MFMA A-operand lane order, and a token tile is gathered
-// row by row straight into B-operand lane order, so all LDS reads are
-// conflict-free ds_read_b128.  Per k-step: wait for this wave's loads of the
-// stage, barrier (all waves' token loads landed, and the slot of the previous
-// stage is free), issue the loads of the stage NS-1 ahead into that slot,
-// multiply.  Token fragments past the block's rows are skipped.
+// Pipeline, one 32-wide k-step per stage.  The token tile of a stage is
+// shared by all waves: it is gathered row by row straight into B-operand lane
+// order in an NS-slot LDS ring by global_load_lds_dwordx4 (lane l's 16 bytes
+// land at tile base + 16 l), so LDS reads are conflict-free ds_read_b128.
+// Each weight fragment is used by one wave only, so weights skip LDS: a
+// packed weight tile is one contiguous kilobyte already in A-operand lane
+// order and goes straight into a 4-slot register ring, NS-1 steps ahead.
+// Token operands are double-buffered in registers (the LDS reads of step k+1
+// overlap the MFMAs of step k).  Token fragments past the block's rows are
+// skipped.
 //
 // XCD-aware order: block b runs on XCD b % 8; work items are dealt so that
-// each XCD walks a contiguous range of (row block, weight tile) items, which
-// keeps a row block's token rows (and repeated weight tiles of one expert's
-// consecutive row blocks) in that XCD's L2.
+// each XCD walks a contiguous range of items ordered (group, weight tile,
+// row block).  Workgroups that run side by side on one XCD then share weight
+// tiles (across an expert's row blocks) and token rows (across weight tiles),
+// and since they advance through K at about the same pace, each k-step's
+// tiles are fetched from HBM once and served to the others from L2.
 #include "smoe_internal.h"
+
+#include <type_traits>
+
+#ifndef SMOE_LDS_STAGES
+#define SMOE_LDS_STAGES 4
+#endif
 
 namespace smoe {
 
@@ -64,36 +73,43 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
+// s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS read of this wave is done.
+template <int N>
+__device__ inline void wait_vmcnt_lds() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | (((N >> 4) & 3) << 14));
+}
+
 template <int MODE, int NB, int NS>
 __global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
   constexpr int FRW = 4;                  // weight fragments per wave
   constexpr int NBW = NB / 4;             // token fragments each wave loads
   static_assert(NB % 4 == 0, "token fragments are loaded 4 ways");
-  constexpr int STAGE_A = 4 * FRW * 1024; // bytes of weight tiles per stage
-  constexpr int STAGE = STAGE_A + NB * 1024;
-  constexpr int LOADS = FRW + NBW;        // loads per wave per stage
-  static_assert(NS == 4 || NS == 5, "the k-loop below is unrolled for 4- or 5-slot rings");
-  // one array per ring slot: the compiler can tell the slot being filled
-  // from the slot being read, so it adds no waits of its own between them
-  __shared__ __attribute__((aligned(1024))) unsigned char ring0[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char ring1[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char ring2[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char ring3[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char ring4[NS == 5 ? STAGE : 16];
+  constexpr int STAGE = NB * 1024;         // bytes of token tiles per stage
+  constexpr int LOADS = FRW + NBW;        // vector-memory ops per wave per stage
+  static_assert(NS % 2 == 0 && NS >= 4 && NS <= 8, "ring of 4, 6 or 8 slots");
+  static_assert(LOADS * (NS - 1) < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS][STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
 
-  // XCD-aware deal of (row block, weight tile) work items
+  // XCD-aware deal of work items; items run in (group, weight tile, row
+  // block) order, so the row blocks that share a weight tile and the tiles
+  // that share a row block run side by side on one XCD and meet in its L2
   const int n_items = *P.n_rb * P.tiles;
   const int per = (n_items + 7) >> 3;
   const int slot_b = blockIdx.x >> 3;
   if (slot_b >= per) return;
   const int item = (blockIdx.x & 7) * per + slot_b;
   if (item >= n_items) return;
-  const int rbi = item / P.tiles;
-  const int tile = item - rbi * P.tiles;
+  // a group's items fill [first * tiles, (first + n_group) * tiles)
+  const RowBlock any = P.rb[item / P.tiles];
+  const int local = item - any.first * P.tiles;
+  const int tile = local / any.n_group;
+  const int rbi = any.first + (local - tile * any.n_group);
+  if (rbi >= *P.n_rb) return;
   const RowBlock blk = P.rb[rbi];
   const bool shared = blk.group == P.E;
   const int inter = shared ? P.Is : P.I;
@@ -138,87 +154,104 @@ __global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
     tsrc[i] = base + 8 * g;
   }
 
-  auto issue = [&](unsigned char* st, int step) {
-    const int ks = min(step, nsteps - 1);   // past the end: harmless re-load
-#pragma unroll
-    for (int f = 0; f < FRW; ++f)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(wsrc[f] + (size_t)ks * 512),
-                                       (lds_void_t*)(st + (wave * FRW + f) * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < NBW; ++i)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(tsrc[i] + ks * 32),
-                                       (lds_void_t*)(st + STAGE_A + (wave * NBW + i) * 1024), 16,
-                                       0, 0);
-  };
-
   f32x4 acc[FRW][NB];
 #pragma unroll
   for (int f = 0; f < FRW; ++f)
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const unsigned char* st) {
-    // all fragment reads first (fragments past the block hold valid repeated
-    // rows), then the MFMAs of the fragments with real rows
-    u32x4 a[FRW], b[NB];
+  // past the end of K every load re-reads the last step (harmless, in bounds)
+  auto load_w = [&](u32x4 (&a)[FRW], int step) {
+    const int ks = min(step, nsteps - 1);
 #pragma unroll
     for (int f = 0; f < FRW; ++f)
-      a[f] = *reinterpret_cast<const u32x4*>(st + (wave * FRW + f) * 1024 + lane * 16);
+      a[f] = *reinterpret_cast<const u32x4*>(wsrc[f] + (size_t)ks * 512);
+  };
+  auto load_t = [&](unsigned char* st, int step) {
+    const int ks = min(step, nsteps - 1);
+#pragma unroll
+    for (int i = 0; i < NBW; ++i)
+      __builtin_amdgcn_global_load_lds((glob_void_t*)(tsrc[i] + ks * 32),
+                                       (lds_void_t*)(st + (wave * NBW + i) * 1024), 16, 0, 0);
+  };
+  auto read_t = [&](const unsigned char* st, u32x4 (&b)[NB]) {
+    // fragments past the block hold valid repeated rows; their MFMAs are skipped
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
-      b[nb] = *reinterpret_cast<const u32x4*>(st + STAGE_A + nb * 1024 + lane * 16);
-    __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the MFMAs
+      b[nb] = *reinterpret_cast<const u32x4*>(st + nb * 1024 + lane * 16);
+  };
+  auto mma = [&](const u32x4 (&a)[FRW], const u32x4 (&b)[NB]) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       if (nb < nb_act) {
 #pragma unroll
         for (int f = 0; f < FRW; ++f)
           acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, a[f]), __builtin_bit_cast(bf16x8, b[nb]), acc[f][nb], 0,
-              0, 0);
+              __builtin_bit_cast(bf16x8, a[f]), __builtin_bit_cast(bf16x8, b[nb]), acc[f][nb],
+              0, 0, 0);
       }
     }
   };
-  // one k-step: this wave's loads of the step have landed (the NS-2 later
-  // stages may still be in flight); the barrier makes everyone's visible and
-  // frees the slot read one step earlier, which then takes the step NS-1 ahead
-  auto step = [&](unsigned char* cur, unsigned char* next_free, int k) {
-    wait_vmcnt<LOADS * (NS - 2)>();
+  // One k-step (j = k mod NS, a compile-time slot index).  Step k issues the
+  // weights of step k+NS-1 and the tokens of step k+NS.  The tokens of step
+  // k+1 were issued NS-1 steps ago, so exactly NS-2 steps' ops are younger:
+  // the wait below completes the weights of step k and the tokens of step
+  // k+1 (and, lgkmcnt(0), this wave's LDS reads of step k).  The barrier then
+  // makes everyone's token tile k+1 visible and frees slot j for step k+NS.
+  u32x4 w[NS][FRW];
+  u32x4 t[2][NB];
+  auto step = [&](auto jc, int k) {
+    constexpr int j = decltype(jc)::value;
+    wait_vmcnt_lds<LOADS * (NS - 2)>();
     __builtin_amdgcn_s_barrier();
-    issue(next_free, k + NS - 1);
-    compute(cur);
+    __builtin_amdgcn_sched_barrier(0);  // this step's loads stay after the wait
+    load_w(w[(j + NS - 1) % NS], k + NS - 1);
+    load_t(ring[j], k + NS);
+    read_t(ring[(j + 1) % NS], t[(j + 1) % 2]);
+    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
+    mma(w[j], t[j % 2]);
   };
 
+  // prologue, issued in this exact order (scheduling barriers keep the
+  // compiler from interleaving the groups): T0 W0 T1 W1 ... T(NS-2) W(NS-2) T(NS-1)
+#pragma unroll
+  for (int s2 = 0; s2 < NS - 1; ++s2) {
+    load_t(ring[s2], s2);
+    load_w(w[s2], s2);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  load_t(ring[NS - 1], NS - 1);
+  __builtin_amdgcn_sched_barrier(0);
+  // T0 and W0 are the LOADS oldest ops: wait until the rest remain
+  wait_vmcnt_lds<LOADS * (NS - 2) + NBW>();
+  __builtin_amdgcn_s_barrier();
+  read_t(ring[0], t[0]);
   int k = 0;
-  if constexpr (NS == 4) {
-    issue(ring0, 0);
-    issue(ring1, 1);
-    issue(ring2, 2);
-    for (; k + 4 <= nsteps; k += 4) {
-      step(ring0, ring3, k);
-      step(ring1, ring0, k + 1);
-      step(ring2, ring1, k + 2);
-      step(ring3, ring2, k + 3);
+  for (; k + NS <= nsteps; k += NS) {
+    step(std::integral_constant<int, 0>{}, k);
+    step(std::integral_constant<int, 1>{}, k + 1);
+    step(std::integral_constant<int, 2>{}, k + 2);
+    step(std::integral_constant<int, 3>{}, k + 3);
+    if constexpr (NS > 4) {
+      step(std::integral_constant<int, 4 % NS>{}, k + 4);
+      step(std::integral_constant<int, 5 % NS>{}, k + 5);
     }
-    if (k < nsteps) step(ring0, ring3, k);
-    if (k + 1 < nsteps) step(ring1, ring0, k + 1);
-    if (k + 2 < nsteps) step(ring2, ring1, k + 2);
-  } else {
-    issue(ring0, 0);
-    issue(ring1, 1);
-    issue(ring2, 2);
-    issue(ring3, 3);
-    for (; k + 5 <= nsteps; k += 5) {
-      step(ring0, ring4, k);
-      step(ring1, ring0, k + 1);
-      step(ring2, ring1, k + 2);
-      step(ring3, ring2, k + 3);
-      step(ring4, ring3, k + 4);
+    if constexpr (NS > 6) {
+      step(std::integral_constant<int, 6 % NS>{}, k + 6);
+      step(std::integral_constant<int, 7 % NS>{}, k + 7);
     }
-    if (k < nsteps) step(ring0, ring4, k);
-    if (k + 1 < nsteps) step(ring1, ring0, k + 1);
-    if (k + 2 < nsteps) step(ring2, ring1, k + 2);
-    if (k + 3 < nsteps) step(ring3, ring2, k + 3);
+  }
+  // tail: the remaining steps continue the same slot sequence
+  if (k < nsteps) step(std::integral_constant<int, 0>{}, k);
+  if (k + 1 < nsteps) step(std::integral_constant<int, 1>{}, k + 1);
+  if (k + 2 < nsteps) step(std::integral_constant<int, 2>{}, k + 2);
+  if constexpr (NS > 4) {
+    if (k + 3 < nsteps) step(std::integral_constant<int, 3>{}, k + 3);
+    if (k + 4 < nsteps) step(std::integral_constant<int, 4 % NS>{}, k + 4);
+  }
+  if constexpr (NS > 6) {
+    if (k + 5 < nsteps) step(std::integral_constant<int, 5 % NS>{}, k + 5);
+    if (k + 6 < nsteps) step(std::integral_constant<int, 6 % NS>{}, k + 6);
   }
   wait_vmcnt<0>();  // no LDS write may be in flight when the workgroup ends
 
@@ -278,7 +311,7 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
   gp.row_token = a.row_token; gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.h;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.gu_tiles;
   gp.limit = a.limit; gp.limit_shared = a.limit_shared;
-  hipLaunchKernelGGL((expert_gemm_lds_kernel<0, 12, 4>), dim3(lds_grid(p, p.gu_tiles)), dim3(256),
+  hipLaunchKernelGGL((expert_gemm_lds_kernel<0, 12, SMOE_LDS_STAGES>), dim3(lds_grid(p, p.gu_tiles)), dim3(256),
                      0, s, gp);
   return hipGetLastError();
 }
@@ -288,7 +321,7 @@ hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
   gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.o;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.dn_tiles;
-  hipLaunchKernelGGL((expert_gemm_lds_kernel<1, 12, 4>), dim3(lds_grid(p, p.dn_tiles)), dim3(256),
+  hipLaunchKernelGGL((expert_gemm_lds_kernel<1, 12, SMOE_LDS_STAGES>), dim3(lds_grid(p, p.dn_tiles)), dim3(256),
                      0, s, gp);
   return hipGetLastError();
 }

@@ -331,14 +331,14 @@ __device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int ha
     offsets[tid] = off;
     for (int i = 0; i < nrb; ++i) {
       const int p = rbpos + i;
-      if (p < rb_max) rb[p] = RowBlock{tid, off + i * bn, min(bn, cnt - i * bn), 0};
+      if (p < rb_max) rb[p] = RowBlock{tid, off + i * bn, min(bn, cnt - i * bn), rbpos, nrb, {0, 0, 0}};
     }
   }
   if (tid == 0) offsets[E] = total;
   const int nrb_s = has_shared ? (T + bn - 1) / bn : 0;
   for (int i = tid; i < nrb_s; i += blockDim.x) {
     const int p = rb_total + i;
-    if (p < rb_max) rb[p] = RowBlock{E, KT + i * bn, min(bn, T - i * bn), 0};
+    if (p < rb_max) rb[p] = RowBlock{E, KT + i * bn, min(bn, T - i * bn), rb_total, nrb_s, {0, 0, 0}};
   }
   if (tid == 0) n_rb[0] = min(rb_total + nrb_s, rb_max);
   return off;

@@ -15,12 +15,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // One row block of the grouped GEMMs: `n_rows` consecutive rows (in the
 // expert-contiguous row order) that belong to `group` (an expert id, or E for
-// the shared expert), starting at global row `row_start`.
+// the shared expert), starting at global row `row_start`.  The blocks of one
+// group are consecutive in the list: `first` is the index of the group's
+// first block and `n_group` the number of its blocks.
 struct RowBlock {
   int32_t group;
   int32_t row_start;
   int32_t n_rows;
-  int32_t pad;
+  int32_t first;
+  int32_t n_group;
+  int32_t pad[3];
 };
 
 // ---------------------------------------------------------------- tiling plan

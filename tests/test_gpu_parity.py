@@ -251,3 +251,50 @@ def test_pack_layout_bit_exact():
                 off = m * R * C + (rt * (C // 32) + kt) * 512 + 8 * (16 * (c // 8) + r) + c % 8
                 want[off] = src[m, row, col]
     assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- chained layers
+def test_flash_long_chain_teacher_forced_sampled():
+    """Four chained Flash-shaped layers at T=32768 (the long-context prefill
+    chunk): every GPU step is checked against the oracle fed the GPU's own
+    input of that step (teacher forcing): the norm on sampled rows, the
+    routing bit-exactly on every token (R1) and by the margin rule on sampled
+    tokens (R2/R3), the layer output on sampled rows, and the residual add
+    on every row."""
+    wl = WORKLOADS["long"]
+    inp = make_inputs(wl, device=DEV)
+    layers = []
+    for li, L in enumerate(inp.layers):
+        layers.append(B.MoELayer(inp.router_ws[li], inp.router_bs[li], L.w_gate, L.w_up, L.w_down,
+                                 L.ws_gate, L.ws_up, L.ws_down, K=wl.K, T_max=wl.T))
+    chain = B.MoEChain(layers)
+    r_final, trace = chain.forward(inp.x, capture=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    T = wl.T
+    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 14, replace=False)]))
+    route_rows = np.unique(np.concatenate([rows, rng.choice(T, 242, replace=False)]))
+    for li, (r_l, x_l, y_l, rt) in enumerate(trace):
+        print(f"layer {li}", flush=True)
+        L = inp.layers[li]
+        Wr, b = host_f64(inp.router_ws[li]), host_f64(inp.router_bs[li])
+        r_rows = host_f64(r_l[torch.as_tensor(route_rows, device=DEV)])
+        x_rows = host_f64(x_l[torch.as_tensor(route_rows, device=DEV)])
+        check_output(x_rows, oracle.rmsnorm(r_rows, 1e-6), f"norm {li}")
+        rg = gpu_routing_np(rt)
+        # R1 on every token; R2/R3 on the sampled tokens
+        ref = oracle.route(x_rows, Wr, b, wl.K)
+        check_routing(rg, ref, wl.K, wl.E, b, tokens=route_rows)
+        sel = rg["topk_idx"].astype(np.int64)[rows]
+        xs = host_f64(x_l[torch.as_tensor(rows, device=DEV)])
+        yref = oracle.moe_layer(xs, Wr, b, LazyStack(L.w_gate), LazyStack(L.w_up),
+                                LazyStack(L.w_down), host_f64(L.ws_gate), host_f64(L.ws_up),
+                                host_f64(L.ws_down), K=wl.K, sel=sel)
+        ys = host_f64(y_l[torch.as_tensor(rows, device=DEV)])
+        res = check_output(ys, yref, f"layer {li} output")
+        print(f"  rows={len(rows)} max_rel={res[0]:.3e} l2_rel={res[1]:.3e}", flush=True)
+        r_next = trace[li + 1][0] if li + 1 < len(trace) else r_final
+        rn = r_next.float()
+        want = r_l.float() + y_l.float()
+        err = (rn - want).abs().max().item()
+        assert err <= want.abs().max().item() * 2 ** -8, f"residual {li}: {err}"
