@@ -88,20 +88,90 @@ def _src_sha(paths):
     return h.hexdigest()[:16]
 
 
-GEMM_SOURCES = ["sparse_moe_transformer_fp32_amd/csrc/expert_gemm.hip",
-                "sparse_moe_transformer_fp32_amd/csrc/api.cpp"]
+_CSRC = "sparse_moe_transformer_fp32_amd/csrc/"
+# sources that define each measured kernel and its launch configuration
+KERNEL_SOURCES = {
+    "decode": [_CSRC + "expert_gemm.hip", _CSRC + "api.cpp", _CSRC + "smoe_internal.h"],
+    "prefill": [_CSRC + "expert_gemm_lds.hip", _CSRC + "api.cpp", _CSRC + "smoe_internal.h"],
+}
+KERNEL_SOURCES["long"] = KERNEL_SOURCES["skew"] = KERNEL_SOURCES["prefill"]
+KERNEL_SOURCES["skew_mild"] = KERNEL_SOURCES["prefill"]
 
 
 def _traffic(kernel_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+    """HBM bytes per launch (fetch + write, calibrated) from the committed
+    rocprofv3 counter record, or None when the kernel's sources changed since
+    the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(kernel_key)
-    if not rec or rec.get("source_sha") != _src_sha(GEMM_SOURCES):
+    wl = kernel_key.split(":")[1]
+    if not rec or rec.get("source_sha") != _src_sha(KERNEL_SOURCES[wl]):
         return None
     return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- offline helpers
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_stats(csv_path, out_path, command, regex="smoe"):
+    """Short text summary of a rocprofv3 --stats kernel table."""
+    rows = [r for r in _read_csv(csv_path) if re.search(regex, r["Name"])]
+    lines = [f"# rocprofv3 kernel statistics ({os.path.basename(csv_path)})",
+             f"# command: {command}",
+             f"# kernels matching /{regex}/; durations in microseconds",
+             f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10}  kernel"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}  {r['Name']}")
+    with open(out_path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def write_traffic(pmc_root, commands):
+    """From rocprofv3 --pmc runs laid out as <pmc_root>/<name>_<COUNTER>/
+    run_counter_collection.csv for name in copy/decode/prefill, compute the
+    per-dispatch HBM bytes of the gate/up kernel, scaled by what the same
+    counters read for a plain 1 GiB device copy, and record them."""
+    import collections
+    def per_kernel(name, counter):
+        agg = collections.defaultdict(list)
+        for r in _read_csv(os.path.join(pmc_root, f"{name}_{counter}", "run_counter_collection.csv")):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in agg.items()}
+    copy_bytes = 1 << 30
+    cf = max(v for k, v in per_kernel("copy", "FETCH_SIZE").items() if "copy" in k.lower())
+    cw = max(v for k, v in per_kernel("copy", "WRITE_SIZE").items() if "copy" in k.lower())
+    f_fetch, f_write = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    out = {}
+    text = [f"# HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by",
+            f"# a plain 1 GiB device copy: FETCH_SIZE read {cf:.0f} KiB -> factor {f_fetch:.4f};",
+            f"# WRITE_SIZE read {cw:.0f} KiB -> factor {f_write:.4f}.", "# commands:"]
+    text += [f"#   {c}" for c in commands]
+    for wl in ("decode", "prefill"):
+        fe, wr = per_kernel(wl, "FETCH_SIZE"), per_kernel(wl, "WRITE_SIZE")
+        for k in sorted(fe):
+            if "smoe" not in k:
+                continue
+            b = fe[k] * 1024 * f_fetch + wr.get(k, 0.0) * 1024 * f_write
+            text.append(f"{wl:8s} fetch {fe[k] * 1024 * f_fetch / 1e9:9.4f} GB  write "
+                        f"{wr.get(k, 0.0) * 1024 * f_write / 1e9:9.4f} GB  {k}")
+            if "expert_gemm" in k and ("<0," in k):   # gate/up + SwiGLU
+                out[f"gate_up:{wl}"] = {"kernel": k, "bytes_per_launch": int(b),
+                                        "fetch_kib": fe[k], "write_kib": wr.get(k, 0.0),
+                                        "fetch_factor": f_fetch, "write_factor": f_write,
+                                        "source_sha": _src_sha(KERNEL_SOURCES[wl])}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    with open(os.path.join(ROOT, "profiles", "hbm_bytes_gate_up_down_decode_prefill.txt"), "w") as f:
+        f.write("\n".join(text) + "\n")
+    print("\n".join(text))
 
 
 def layer_work(wl, counts):
@@ -239,7 +309,17 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--summarize-stats", nargs=3, metavar=("CSV", "OUT", "COMMAND"),
+                    help="offline: write a short summary of a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--write-traffic", nargs="+", metavar="ARG",
+                    help="offline: PMC_ROOT COMMAND... -> profiles/traffic.json")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(*args.summarize_stats)
+        return
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1:])
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; --gpus must be 1.",
               file=sys.stderr)
@@ -262,12 +342,13 @@ def main():
     tok_s = wl.T / (ms / 1e3)
     gu_ms = res["stage_ms"]["gate_up"]
     nl = res["n_layers"]
+    tkey = f"gate_up:{wl.name}" if wl.name in ("decode", "prefill") else None
     if wl.T <= 64:   # weight streaming: HBM bound
         rf = roofline_obj("hbm", work["gu_bytes"] / (gu_ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s",
-                          _traffic(f"gate_up:{wl.name}"))
+                          _traffic(tkey) if tkey else None)
     else:
         rf = roofline_obj("mfma", work["gu_flops"] / (gu_ms * 1e-3) / 1e12,
-                          MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", _traffic(f"gate_up:{wl.name}"))
+                          MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", _traffic(tkey) if tkey else None)
     layer_ms = ms / nl
     line = {
         "metric": "MoE-layer tokens/s + % roofline (HBM GB/s @T=16, MFMA TFLOP/s @T=4096)",
