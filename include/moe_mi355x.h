@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -135,6 +135,33 @@ typedef struct {
   float* scores;
 } moe_routing;
 
+/* The residual stream around one layer, for moe_forward_residual (host
+ * struct of device pointers).  Pre-norm reading of paperlayer.ai summary,
+ * App. B (the final representation is the sum of the layer outputs followed
+ * by RMSNorm) with the model card's zero_centered gain:
+ *   r_in    [T,H] bf16  residual stream entering the layer (non-NULL)
+ *   r_out   [T,H] bf16  receives r_in + layer output, rounded once to bf16
+ *                       (non-NULL; may alias r_in)
+ *   x_next  [T,H] bf16  NULL, or receives the next layer's input
+ *                       bf16(r / sqrt(mean(r^2) + eps) * (1 + gamma)), r the
+ *                       stored bf16 r_out row; must not alias r_in or r_out
+ *                       (it may alias the layer's own x)
+ *   gamma   [H] fp32    zero-centred gain of that norm, or NULL (gain 1)
+ *   eps                 finite, >= 0 */
+typedef struct {
+  const uint16_t* r_in;
+  uint16_t* r_out;
+  uint16_t* x_next;
+  const float* gamma;
+  float eps;
+} moe_residual;
+
+/* A dense gated FFN (the model's first, dense layers), bf16, PACKED:
+ * w_gate [I,H], w_up [I,H] as one packed matrix each; w_down as S packed
+ * matrices [H, I/S], matrix s being columns s*I/S .. (s+1)*I/S - 1 of the
+ * model's Wd [H,I] (see moe_dense_ffn). */
+typedef moe_shared moe_ffn;
+
 /* Byte offsets of the intermediates inside a workspace (host struct), for
  * inspection by tests.  h is bf16 [(T*K)*I + T*Is]: routed rows of width I
  * in expert-contiguous order, then the shared expert's T rows of width Is.
@@ -203,6 +230,17 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
 moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, int32_t rows,
                             int32_t cols, hipStream_t stream);
 
+/* moe_pack_weights with a strided source: element (i, j) of source matrix m
+ * is src[m*mat_stride + i*ld + j] (elements).  ld >= cols; ld and
+ * mat_stride multiples of 8.  moe_pack_weights is the case ld = cols,
+ * mat_stride = rows*cols.  Column slices of one wide matrix are packed with
+ * mat_stride = the slice width, as moe_dense_ffn's w_down needs: Wd [H,I]
+ * into S matrices [H, I/S] is n_mats = S, rows = H, cols = I/S, ld = I,
+ * mat_stride = I/S.  dst receives n_mats packed [rows, cols] matrices. */
+moe_status moe_pack_weights_strided(const uint16_t* src, uint16_t* dst, int32_t n_mats,
+                                    int32_t rows, int32_t cols, int64_t ld, int64_t mat_stride,
+                                    hipStream_t stream);
+
 /* Glue between chained layers of a pre-norm residual stream (paperlayer.ai
  * summary, App. B: RMSNorm over the summed layer outputs; model card:
  * zero_centered).  For each of the T rows of width H:
@@ -215,6 +253,63 @@ moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, 
 moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
                                 const uint16_t* y_add, const float* gamma, float eps,
                                 uint16_t* r_out, uint16_t* x_out, hipStream_t stream);
+
+/* The whole layer followed by the residual add and, optionally, the next
+ * layer's norm (the combine, the add and the norm run as one kernel):
+ *   r_out[t]  = bf16( r_in[t] + (sum_j w[t,j] FFN_{sel_j}(x[t]) + FFN_shared(x[t])) )
+ *   x_next[t] = bf16( r_out[t] / sqrt(mean(r_out[t]^2) + eps) * (1 + gamma) )
+ * The layer output is summed in fp32 in slot order (shared last) and added
+ * to r_in in fp32 before the one rounding, so it is never stored on its own.
+ * x is the layer's (already normalised) input; it must not alias r_in or
+ * r_out.  Other arguments, the workspace and the errors are as for
+ * moe_forward; res and its r_in, r_out must be non-NULL. */
+moe_status moe_forward_residual(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                                const moe_router* router, const moe_experts* experts,
+                                const moe_shared* shared, const moe_residual* res,
+                                const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Workspace bytes for moe_dense_ffn (host); 0 if the sizes are out of range. */
+size_t moe_dense_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t S);
+
+/* A dense gated FFN, y[t] = Wd (silu(Wg x[t]) * (Wu x[t])) (hyper.ai summary,
+ * 方法, and paperlayer.ai summary, §2.2: the first three of the 45 layers
+ * are dense; model card: intermediate_size 11264).  The intermediate
+ * dimension is cut into S slices that run as S groups of the grouped
+ * expert GEMMs, every token in every group with weight 1; the S partial
+ * outputs of a token are rounded to bf16 and added in fp32 in slice order,
+ * then rounded once more.
+ *   T, H     as in moe_dims
+ *   I        intermediate size; I/S must be a multiple of 64, <= 16384
+ *   S        slices, 1 <= S <= 16; T*S <= 1<<24.  w_down must have been
+ *            packed for the same S.  More slices give small batches more
+ *            workgroups (S = 8 for I = 11264).
+ *   ffn      packed weights (moe_ffn above)
+ *   swiglu_limit  as moe_opts.swiglu_limit (0 = off)
+ *   y        [T,H] bf16 output, must not alias x
+ *   ws       device workspace of ws_bytes >= moe_dense_workspace_bytes */
+moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint16_t* x,
+                         const moe_ffn* ffn, float swiglu_limit, uint16_t* y, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
+/* Per-expert activation statistics for monitoring (paperlayer.ai summary,
+ * §4.1.2 and §4.1.3: per-expert activation norms, whose maximum-to-median
+ * ratio exposes localized blow-up and whose falling minimum-to-median ratio
+ * warns of expert death; App. B: the blow-up is in the SwiGLU product h).
+ * Reads h and offsets of a finished moe_forward / moe_forward_residual call
+ * with the same d: h at workspace offset moe_ws_layout.h, offsets from the
+ * routing output (or the caller's copy).  With ||h_r|| the L2 norm of row r
+ * of h (bf16 values, squares summed in fp32), for each routed expert g < E,
+ * then the shared expert g = E when d->Is > 0:
+ *   stats[4g..4g+3] = { rows, sum ||h_r||, sum ||h_r||^2, max ||h_r|| }  fp32
+ * and, when ratios is non-NULL, over the routed experts with rows, m_e =
+ * stats[4e+1] / stats[4e] and M their median (mean of the two middle values
+ * for an even count):
+ *   ratios[0] = max m_e / M,  ratios[1] = min m_e / M                   fp32
+ * stats has 4*(E+1) floats (4*E without a shared expert), ratios 2.
+ * Deterministic (fixed-order sums).  Errors as for moe_forward. */
+moe_status moe_expert_stats(const moe_dims* d, const int32_t* offsets, const uint16_t* h,
+                            float* stats, float* ratios, hipStream_t stream);
 
 /* Per-stage timing hook for benchmarks and profilers (thread-local, host).
  * `events` is a host array of 2*MOE_N_STAGES hipEvent_t created by the

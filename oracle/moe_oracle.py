@@ -44,6 +44,16 @@ constant below):
   A15 RMSNorm epsilon 1e-6, zero-centred gain (1 + gamma).
   Ties between equal keys go to the lower expert index.
 
+  [P3 4.1.2], [P3 4.1.3]  paperlayer.ai summary, §4.1.2 (expert collapse:
+               monitor per-expert activation norms; a falling
+               minimum-to-median ratio warns of expert death) and §4.1.3
+               (localized activation blow-up: the maximum-to-median
+               activation-norm ratio exposes it).
+  A18 an expert's activation norm is the L2 norm of a token's SwiGLU
+      activation h (the product the blow-up appears in); per expert the
+      mean over the tokens routed to it; the ratios compare those means
+      over the experts with tokens, against their median.
+
 Parity status: every function here is pinned by the CPU tests (dense brute
 force, closed forms, invariants, hand-computed cases); none is unpinned.
 """
@@ -55,8 +65,9 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64", "router_logits", "router_scores", "selection_keys",
-    "select_topk", "routing_weights", "dispatch", "swiglu_ffn", "route",
-    "moe_layer", "rmsnorm", "moe_chain",
+    "select_topk", "routing_weights", "dispatch", "swiglu_hidden", "swiglu_ffn", "route",
+    "moe_layer", "rmsnorm", "moe_chain", "dense_ffn", "activation_stats", "norm_ratios",
+    "expert_activation_stats",
 ]
 
 
@@ -165,12 +176,10 @@ def silu(z) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
 
-def swiglu_ffn(xr, Wg, Wu, Wd, return_hidden: bool = False, limit: float = 0.0):
-    """One gated expert on rows xr [m, H]: h = silu(xr Wg^T) * (xr Wu^T),
-    o = h Wd^T.  Wg, Wu are [I, H]; Wd is [H, I].  [P3 App.B]: SwiGLU, the
-    product of the gate and up activations; the three matrices of size
-    4096 x 1280 per expert are what the 196B/11B parameter counts of
-    [P3 2.2] add up to.
+def swiglu_hidden(xr, Wg, Wu, limit: float = 0.0) -> np.ndarray:
+    """The SwiGLU activation of one gated expert on rows xr [m, H]:
+    h = silu(xr Wg^T) * (xr Wu^T), with Wg, Wu [I, H].  [P3 App.B]: the
+    element-wise product of the gate and up activations.
 
     `limit` is [P4 config] swiglu_limits: 0 = no clamp (reading A8, the
     value of almost every layer).  A positive limit clamps the gate
@@ -183,9 +192,66 @@ def swiglu_ffn(xr, Wg, Wu, Wd, return_hidden: bool = False, limit: float = 0.0):
     if limit > 0:
         g = np.minimum(g, limit)
         u = np.clip(u, -limit, limit)
-    h = silu(g) * u
+    return silu(g) * u
+
+
+def swiglu_ffn(xr, Wg, Wu, Wd, return_hidden: bool = False, limit: float = 0.0):
+    """One gated expert on rows xr [m, H]: o = h Wd^T with h the SwiGLU
+    activation (swiglu_hidden); Wd is [H, I].  The three matrices of size
+    4096 x 1280 per expert are what the 196B/11B parameter counts of
+    [P3 2.2] add up to."""
+    h = swiglu_hidden(xr, Wg, Wu, limit)
     o = h @ _f64(Wd).T
     return (o, h) if return_hidden else o
+
+
+def dense_ffn(x, Wg, Wu, Wd, limit: float = 0.0) -> np.ndarray:
+    """The dense FFN of the model's first layers ([P3 2.2]: 3 dense and 42
+    MoE layers; [P4 config] intermediate_size 11264): the same gated form as
+    an expert, on every token, with no router."""
+    return swiglu_ffn(x, Wg, Wu, Wd, limit=limit)
+
+
+def activation_stats(h) -> np.ndarray:
+    """[rows, sum ||h_r||, sum ||h_r||^2, max ||h_r||] over the rows of one
+    expert's SwiGLU activations h [m, I] (zeros for m = 0).  [P3 4.1.2],
+    [P3 4.1.3]: per-expert activation norms are what is monitored; [P3
+    App.B]: the blow-up is in the SwiGLU product."""
+    h = _f64(h)
+    if h.shape[0] == 0:
+        return np.zeros(4)
+    n = np.sqrt(np.sum(h * h, axis=1))
+    return np.array([h.shape[0], n.sum(), np.sum(n * n), n.max()])
+
+
+def norm_ratios(stats) -> np.ndarray:
+    """[max m_e / M, min m_e / M] over the experts with rows, m_e = mean
+    activation norm (stats[e,1] / stats[e,0]) and M the median of the m_e.
+    [P3 4.1.3]: the maximum-to-median ratio reveals localized blow-up;
+    [P3 4.1.2]: a falling minimum-to-median ratio warns of expert death."""
+    st = _f64(stats)
+    act = st[:, 0] > 0
+    m = st[act, 1] / st[act, 0]
+    med = np.median(m)
+    return np.array([m.max() / med, m.min() / med])
+
+
+def expert_activation_stats(x, sel, Wg, Wu, Ws_g=None, Ws_u=None, limit: float = 0.0,
+                            limit_shared: float = 0.0, E: Optional[int] = None) -> np.ndarray:
+    """activation_stats of every routed expert e < E over the tokens that
+    selected it, then of the shared expert over all tokens (when given):
+    an [E (+1), 4] array."""
+    x = _f64(x)
+    sel = np.asarray(sel, dtype=np.int64)
+    E = int(sel.max()) + 1 if E is None else E
+    rows = []
+    for e in range(E):
+        t = np.nonzero((sel == e).any(axis=1))[0]
+        rows.append(activation_stats(swiglu_hidden(x[t], Wg[e], Wu[e], limit)) if t.size
+                    else np.zeros(4))
+    if Ws_g is not None:
+        rows.append(activation_stats(swiglu_hidden(x, Ws_g, Ws_u, limit_shared)))
+    return np.stack(rows)
 
 
 def route(x, Wr, b, K: int, scale: float = 3.0, norm: bool = True,

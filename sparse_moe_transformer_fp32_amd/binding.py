@@ -15,7 +15,7 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsmoe_gfx950.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_OPTION = 0, -1, -2, -3
 MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_DEVICE = -4, -5, -6
@@ -23,8 +23,9 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
                 -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_DEVICE"}
 
 EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
-            "moe_route", "moe_forward", "moe_residual_rmsnorm", "moe_set_stage_events",
-            "moe_pack_weights"]
+            "moe_route", "moe_forward", "moe_forward_residual", "moe_residual_rmsnorm",
+            "moe_set_stage_events", "moe_pack_weights", "moe_pack_weights_strided",
+            "moe_dense_workspace_bytes", "moe_dense_ffn", "moe_expert_stats"]
 STAGES = ["route_logits", "route_topk", "dispatch", "gate_up", "down", "combine"]
 
 _vp = ctypes.c_void_p
@@ -55,6 +56,11 @@ class Shared(ctypes.Structure):
 class Routing(ctypes.Structure):
     _fields_ = [(n, _vp) for n in ("topk_idx", "topk_w", "counts", "offsets", "perm_token",
                                    "slot_pos", "keys", "scores")]
+
+
+class Residual(ctypes.Structure):
+    _fields_ = [("r_in", _vp), ("r_out", _vp), ("x_next", _vp), ("gamma", _vp),
+                ("eps", ctypes.c_float)]
 
 
 class WsLayout(ctypes.Structure):
@@ -93,6 +99,19 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Experts), P(Shared), _vp,
                                 P(Routing), _vp, ctypes.c_size_t, _vp]
+    lib.moe_forward_residual.restype = ctypes.c_int
+    lib.moe_forward_residual.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Experts), P(Shared),
+                                         P(Residual), P(Routing), _vp, ctypes.c_size_t, _vp]
+    lib.moe_dense_workspace_bytes.restype = ctypes.c_size_t
+    lib.moe_dense_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+    lib.moe_dense_ffn.restype = ctypes.c_int
+    lib.moe_dense_ffn.argtypes = [ctypes.c_int32] * 4 + [_vp, P(Shared), ctypes.c_float, _vp, _vp,
+                                                         ctypes.c_size_t, _vp]
+    lib.moe_expert_stats.restype = ctypes.c_int
+    lib.moe_expert_stats.argtypes = [P(Dims), _vp, _vp, _vp, _vp, _vp]
+    lib.moe_pack_weights_strided.restype = ctypes.c_int
+    lib.moe_pack_weights_strided.argtypes = [_vp, _vp, ctypes.c_int32, ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, _vp]
     lib.moe_residual_rmsnorm.restype = ctypes.c_int
     lib.moe_residual_rmsnorm.argtypes = [ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp,
                                          ctypes.c_float, _vp, _vp, _vp]
@@ -221,6 +240,22 @@ def pack_weights(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.T
     return out
 
 
+def pack_column_slices(w: torch.Tensor, S: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S packed matrices [R, C/S] (moe_pack_weights_strided), matrix s being
+    columns s*C/S .. (s+1)*C/S - 1 of the row-major bf16 matrix w [R, C]."""
+    lib = load()
+    _dev(w, "w", torch.bfloat16)
+    R, C = w.shape
+    if C % S:
+        raise ValueError(f"{C} columns do not split into {S} slices")
+    if out is None:
+        out = torch.empty((S, R, C // S), dtype=w.dtype, device=w.device)
+    _dev(out, "out", torch.bfloat16)
+    _check(lib.moe_pack_weights_strided(_ptr(w), _ptr(out), S, R, C // S, C, C // S,
+                                        _stream(w.device)))
+    return out
+
+
 class MoELayer:
     """One MoE FFN layer bound to device weights, with its workspace and
     output buffer allocated once (calls allocate nothing).  Expert weights
@@ -287,6 +322,96 @@ class MoELayer:
 
     __call__ = forward
 
+    def forward_residual(self, x: torch.Tensor, r_in: torch.Tensor,
+                         r_out: Optional[torch.Tensor] = None,
+                         x_next: Optional[torch.Tensor] = None,
+                         gamma: Optional[torch.Tensor] = None, eps: float = 1e-6,
+                         routing: Optional[Dict[str, torch.Tensor]] = None) -> torch.Tensor:
+        """r_out = r_in + layer(x); x_next (if given) = RMSNorm(r_out)
+        (moe_forward_residual).  r_out may be r_in; x_next may be x."""
+        lib = load()
+        for n, t in (("x", x), ("r_in", r_in)):
+            _dev(t, n, torch.bfloat16)
+        T = x.shape[0]
+        if r_out is None:
+            r_out = torch.empty_like(r_in)
+        _dev(r_out, "r_out", torch.bfloat16)
+        if x_next is not None:
+            _dev(x_next, "x_next", torch.bfloat16)
+        if gamma is not None:
+            _dev(gamma, "gamma", torch.float32)
+        ws_bytes = self.reserve(T)
+        d = dims(T, self.H, self.E, self.K, self.I, self.Is)
+        res = Residual(_ptr(r_in), _ptr(r_out), _ptr(x_next), _ptr(gamma), float(eps))
+        rs = _routing_struct(routing) if routing is not None else None
+        _check(lib.moe_forward_residual(
+            ctypes.byref(d), ctypes.byref(self.opts), _ptr(x), ctypes.byref(self.router),
+            ctypes.byref(self.experts),
+            ctypes.byref(self.shared) if self.shared is not None else None, ctypes.byref(res),
+            ctypes.byref(rs) if rs is not None else None, _ptr(self._ws), ws_bytes,
+            _stream(x.device)))
+        return r_out
+
+    def expert_stats(self, T: int, offsets: torch.Tensor, ratios: bool = True):
+        """Per-expert activation statistics of the last call with T tokens
+        (moe_expert_stats): stats [E (+1 shared), 4] = (rows, sum ||h||,
+        sum ||h||^2, max ||h||) and ratios [2] = (max/median, min/median of
+        the mean norms)."""
+        lib = load()
+        _dev(offsets, "offsets", torch.int32)
+        lay = workspace_layout(T, self.H, self.E, self.K, self.I, self.Is)
+        G = self.E + (1 if self.Is else 0)
+        stats = torch.empty((G, 4), dtype=torch.float32, device=self.device)
+        rat = torch.empty(2, dtype=torch.float32, device=self.device) if ratios else None
+        d = dims(T, self.H, self.E, self.K, self.I, self.Is)
+        h_ptr = ctypes.c_void_p(self._ws.data_ptr() + lay.h)
+        _check(lib.moe_expert_stats(ctypes.byref(d), _ptr(offsets), h_ptr, _ptr(stats), _ptr(rat),
+                                    _stream(self.device)))
+        return (stats, rat) if ratios else stats
+
+
+class DenseFFN:
+    """A dense gated FFN y = Wd (silu(Wg x) * (Wu x)) run by moe_dense_ffn
+    with its intermediate dimension cut into S slices.  Weights are given
+    row-major (Wg, Wu [I,H]; Wd [H,I]) and packed once here."""
+
+    def __init__(self, w_gate, w_up, w_down, S: int = 8, T_max=None, swiglu_limit: float = 0.0):
+        load()
+        for n, t in (("w_gate", w_gate), ("w_up", w_up), ("w_down", w_down)):
+            _dev(t, n, torch.bfloat16)
+        self.I, self.H = w_gate.shape
+        self.S = int(S)
+        self.tensors = (pack_weights(w_gate), pack_weights(w_up),
+                        pack_column_slices(w_down, self.S))
+        self.ffn = Shared(*[_ptr(t) for t in self.tensors])
+        self.limit = float(swiglu_limit)
+        self.device = w_gate.device
+        self._ws = None
+        if T_max:
+            self.reserve(T_max)
+
+    def reserve(self, T: int) -> int:
+        need = load().moe_dense_workspace_bytes(T, self.H, self.I, self.S)
+        if need == 0:
+            raise MoEError(MOE_ERR_SHAPE, last_error())
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return need
+
+    def forward(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        lib = load()
+        _dev(x, "x", torch.bfloat16)
+        T = x.shape[0]
+        ws_bytes = self.reserve(T)
+        if y is None:
+            y = torch.empty_like(x)
+        _dev(y, "y", torch.bfloat16)
+        _check(lib.moe_dense_ffn(T, self.H, self.I, self.S, _ptr(x), ctypes.byref(self.ffn),
+                                 self.limit, _ptr(y), _ptr(self._ws), ws_bytes, _stream(x.device)))
+        return y
+
+    __call__ = forward
+
 
 def forward(x, router_w, router_b, w_gate, w_up, w_down, ws_gate=None, ws_up=None, ws_down=None,
             K=8, routing: bool = False, keys: bool = False, **opts):
@@ -332,9 +457,11 @@ def residual_rmsnorm(r_in: torch.Tensor, y_add: Optional[torch.Tensor] = None,
 class MoEChain:
     """Pre-norm residual stream through chained MoE layers:
         x_0 = RMSNorm(r_0);  r_{l+1} = r_l + MoE_l(x_l);  x_{l+1} = RMSNorm(r_{l+1})
-    with one moe_residual_rmsnorm call at each layer boundary (residual add
-    and the next layer's norm together).  Returns the last residual stream.
-    Buffers are allocated once per batch size."""
+    One moe_residual_rmsnorm call makes x_0; then each layer is one
+    moe_forward_residual call, whose last kernel adds the layer output to
+    the stream and, for all but the last layer, writes the next layer's
+    input.  Returns the last residual stream.  Buffers are allocated once per
+    batch size."""
 
     def __init__(self, layers, eps: float = 1e-6, gamma: Optional[torch.Tensor] = None):
         self.layers = list(layers)
@@ -344,29 +471,27 @@ class MoEChain:
 
     def _buffers(self, x):
         if self._bufs is None or self._bufs[0].shape != x.shape:
-            self._bufs = tuple(torch.empty_like(x) for _ in range(4))
+            self._bufs = tuple(torch.empty_like(x) for _ in range(3))
         return self._bufs
 
     def forward(self, r0: torch.Tensor, capture: bool = False,
                 routing_last: Optional[Dict[str, torch.Tensor]] = None):
-        """capture=True also returns, per layer, (r_l, x_l, y_l, routing_l)
+        """capture=True also returns, per layer, (r_l, x_l, routing_l)
         copies (routing with keys and scores) for checking.  routing_last
         receives the last layer's routing."""
-        xn, y, ra, rb = self._buffers(r0)
+        xn, ra, rb = self._buffers(r0)
         trace = []
         residual_rmsnorm(r0, None, self.gamma, self.eps, None, xn, want_r=False)
         r = r0
         for li, lay in enumerate(self.layers):
-            rt = alloc_routing(r0.shape[0], lay.E, lay.K, r0.device, keys=True) if capture else None
-            if rt is None and li == len(self.layers) - 1:
-                rt = routing_last
-            lay.forward(xn, y, rt)
-            if capture:
-                trace.append((r.clone(), xn.clone(), y.clone(), rt))
-            r_next = ra if li % 2 == 0 else rb
             last = li == len(self.layers) - 1
-            residual_rmsnorm(r, y, self.gamma, self.eps, r_next, None if last else xn,
-                             want_x=not last)
+            rt = alloc_routing(r0.shape[0], lay.E, lay.K, r0.device, keys=True) if capture else None
+            if rt is None and last:
+                rt = routing_last
+            if capture:
+                trace.append((r.clone(), xn.clone(), rt))
+            r_next = ra if li % 2 == 0 else rb
+            lay.forward_residual(xn, r, r_next, None if last else xn, self.gamma, self.eps, rt)
             r = r_next
         return (r, trace) if capture else r
 

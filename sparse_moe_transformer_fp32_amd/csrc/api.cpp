@@ -61,6 +61,18 @@ moe_status check_shape(const moe_dims* d) {
   return MOE_OK;
 }
 
+moe_status check_dense(int T, int H, int I, int S) {
+  if (T < 1 || T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T=%d out of range [1, 1048576]", T);
+  if (H < 128 || H > 16384 || H % 128)
+    return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", H);
+  if (S < 1 || S > 16) return fail(MOE_ERR_SHAPE, "S=%d out of range [1, 16]", S);
+  if (I < 64 || I % S || (I / S) % 64 || I / S > 16384)
+    return fail(MOE_ERR_SHAPE, "I=%d must split into S=%d slices that are multiples of 64", I, S);
+  if ((long long)T * S > (1 << 24))
+    return fail(MOE_ERR_SHAPE, "T*S=%lld rows exceed 16777216", (long long)T * S);
+  return MOE_OK;
+}
+
 moe_status check_opts(const moe_opts* o) {
   if (!o) return MOE_OK;
   if (!isfinite(o->route_scale) || o->route_scale <= 0.f)
@@ -289,48 +301,46 @@ moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
   return ok();
 }
 
-moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
-                       const moe_router* router, const moe_experts* experts,
-                       const moe_shared* shared, uint16_t* y, const moe_routing* routing_out,
-                       void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!d || !x || !router || !router->W || !router->b || !experts || !experts->w_gate ||
-      !experts->w_up || !experts->w_down || !y || !ws)
-    return fail(MOE_ERR_NULL,
-                "moe_forward: NULL argument (dims, x, router, router->W/b, experts->w_*, y, ws)");
+}  // extern "C"
+
+namespace {
+
+// Checks shared by moe_forward and moe_forward_residual (null -> shape ->
+// option -> alignment; the workspace is checked by the caller).
+moe_status check_forward(const char* fn, const moe_dims* d, const moe_opts* opts,
+                         const uint16_t* x, const moe_router* router,
+                         const moe_experts* experts, const moe_shared* shared,
+                         const moe_routing* routing_out) {
   moe_status st;
   if (d->Is > 0 && (!shared || !shared->w_gate || !shared->w_up || !shared->w_down))
-    return fail(MOE_ERR_NULL, "moe_forward: Is=%d but the shared expert weights are NULL", d->Is);
+    return fail(MOE_ERR_NULL, "%s: Is=%d but the shared expert weights are NULL", fn, d->Is);
   if (routing_out && (st = check_routing_out(routing_out, false))) return st;
   if ((st = check_shape(d))) return st;
   if ((st = check_opts(opts))) return st;
   if (misaligned(x) || misaligned(router->W) || misaligned(router->b) ||
-      misaligned(experts->w_gate) || misaligned(experts->w_up) || misaligned(experts->w_down) ||
-      misaligned(y) || misaligned(ws))
-    return fail(MOE_ERR_ALIGN, "moe_forward: device pointers must be 16-byte aligned");
+      misaligned(experts->w_gate) || misaligned(experts->w_up) || misaligned(experts->w_down))
+    return fail(MOE_ERR_ALIGN, "%s: device pointers must be 16-byte aligned", fn);
   if (d->Is > 0 && (misaligned(shared->w_gate) || misaligned(shared->w_up) ||
                     misaligned(shared->w_down)))
-    return fail(MOE_ERR_ALIGN, "moe_forward: shared expert pointers must be 16-byte aligned");
+    return fail(MOE_ERR_ALIGN, "%s: shared expert pointers must be 16-byte aligned", fn);
   if (routing_out && (st = check_routing_align(routing_out))) return st;
-  if (x == y) return fail(MOE_ERR_OPTION, "moe_forward: x and y must not alias");
-  smoe::Plan p;
-  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
-  if (ws_bytes < p.ws_total)
-    return fail(MOE_ERR_WORKSPACE, "moe_forward: workspace %zu bytes < required %zu", ws_bytes,
-                p.ws_total);
-  const moe_opts o = opts ? *opts : default_opts();
-  char* w = static_cast<char*>(ws);
-  const RouteBufs rb = routing_out ? bufs_from(routing_out) : bufs_from_ws(p, w);
-  if ((st = run_route(p, o, x, router, rb, w, stream))) return st;
+  return MOE_OK;
+}
 
+// The two grouped GEMMs over the row list already in the workspace.
+moe_status run_experts(const smoe::Plan& p, const moe_opts& o, const uint16_t* x,
+                       const uint16_t* wg, const uint16_t* wu, const uint16_t* wd,
+                       const moe_shared* shared, char* w, uint16_t* out_rows,
+                       hipStream_t stream) {
   const smoe::RowBlock* rbl = reinterpret_cast<const smoe::RowBlock*>(w + p.ws_rb);
   const int32_t* nrb = reinterpret_cast<const int32_t*>(w + p.ws_nrb);
   uint16_t* h = reinterpret_cast<uint16_t*>(w + p.ws_h);
-  uint16_t* ob = reinterpret_cast<uint16_t*>(w + p.ws_o);
-  const bool has_sh = d->Is > 0;
+  const bool has_sh = p.Is > 0;
+  moe_status st;
 
   smoe::GateUpArgs ga{};
-  ga.wg = experts->w_gate;
-  ga.wu = experts->w_up;
+  ga.wg = wg;
+  ga.wu = wu;
   ga.sg = has_sh ? shared->w_gate : nullptr;
   ga.su = has_sh ? shared->w_up : nullptr;
   ga.x = x;
@@ -348,43 +358,194 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
   }
 
   smoe::DownArgs da{};
-  da.wd = experts->w_down;
+  da.wd = wd;
   da.sd = has_sh ? shared->w_down : nullptr;
   da.h = h;
   da.row_w = reinterpret_cast<const float*>(w + p.ws_row_w);
   da.rb = rbl;
   da.n_rb = nrb;
-  da.o = ob;
+  da.o = out_rows;
   {
     StageMark m(MOE_STAGE_DOWN, stream);
     const hipError_t e =
         p.nb == 12 ? smoe::launch_down_lds(p, da, stream) : smoe::launch_down(p, da, stream);
     if ((st = launched(e, "down"))) return st;
   }
-  {
-    StageMark m(MOE_STAGE_COMBINE, stream);
-    if ((st = launched(smoe::launch_combine(p, ob, rb.slot, y, stream), "combine"))) return st;
-  }
+  return MOE_OK;
+}
+
+// moe_forward (res == nullptr: y = layer output) and moe_forward_residual
+// (r_out = r_in + layer output, optionally followed by the next norm).
+moe_status forward_impl(const char* fn, const moe_dims* d, const moe_opts* opts,
+                        const uint16_t* x, const moe_router* router, const moe_experts* experts,
+                        const moe_shared* shared, uint16_t* y, const moe_residual* res,
+                        const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  smoe::Plan p;
+  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
+  if (ws_bytes < p.ws_total)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes,
+                p.ws_total);
+  const moe_opts o = opts ? *opts : default_opts();
+  char* w = static_cast<char*>(ws);
+  const RouteBufs rb = routing_out ? bufs_from(routing_out) : bufs_from_ws(p, w);
+  moe_status st;
+  if ((st = run_route(p, o, x, router, rb, w, stream))) return st;
+  uint16_t* ob = reinterpret_cast<uint16_t*>(w + p.ws_o);
+  if ((st = run_experts(p, o, x, experts->w_gate, experts->w_up, experts->w_down, shared, w, ob,
+                        stream)))
+    return st;
+  StageMark m(MOE_STAGE_COMBINE, stream);
+  const hipError_t e =
+      res ? smoe::launch_combine_residual(p, ob, rb.slot, res->r_in, res->gamma, res->eps,
+                                          res->r_out, res->x_next, stream)
+          : smoe::launch_combine(p, ob, rb.slot, y, stream);
+  if ((st = launched(e, "combine"))) return st;
   return ok();
 }
 
-moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, int32_t rows,
-                            int32_t cols, hipStream_t stream) {
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                       const moe_router* router, const moe_experts* experts,
+                       const moe_shared* shared, uint16_t* y, const moe_routing* routing_out,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (!d || !x || !router || !router->W || !router->b || !experts || !experts->w_gate ||
+      !experts->w_up || !experts->w_down || !y || !ws)
+    return fail(MOE_ERR_NULL,
+                "moe_forward: NULL argument (dims, x, router, router->W/b, experts->w_*, y, ws)");
+  moe_status st;
+  if ((st = check_forward("moe_forward", d, opts, x, router, experts, shared, routing_out)))
+    return st;
+  if (misaligned(y) || misaligned(ws))
+    return fail(MOE_ERR_ALIGN, "moe_forward: device pointers must be 16-byte aligned");
+  if (x == y) return fail(MOE_ERR_OPTION, "moe_forward: x and y must not alias");
+  return forward_impl("moe_forward", d, opts, x, router, experts, shared, y, nullptr, routing_out,
+                      ws, ws_bytes, stream);
+}
+
+moe_status moe_forward_residual(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                                const moe_router* router, const moe_experts* experts,
+                                const moe_shared* shared, const moe_residual* res,
+                                const moe_routing* routing_out, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!d || !x || !router || !router->W || !router->b || !experts || !experts->w_gate ||
+      !experts->w_up || !experts->w_down || !res || !res->r_in || !res->r_out || !ws)
+    return fail(MOE_ERR_NULL,
+                "moe_forward_residual: NULL argument (dims, x, router, router->W/b, "
+                "experts->w_*, res, res->r_in/r_out, ws)");
+  moe_status st;
+  if ((st = check_forward("moe_forward_residual", d, opts, x, router, experts, shared,
+                          routing_out)))
+    return st;
+  if (!isfinite(res->eps) || res->eps < 0.f)
+    return fail(MOE_ERR_OPTION, "moe_forward_residual: eps must be finite and >= 0");
+  if (misaligned(res->r_in) || misaligned(res->r_out) || misaligned(res->x_next) ||
+      misaligned(res->gamma) || misaligned(ws))
+    return fail(MOE_ERR_ALIGN, "moe_forward_residual: device pointers must be 16-byte aligned");
+  if (res->x_next && (res->x_next == res->r_out || res->x_next == res->r_in))
+    return fail(MOE_ERR_OPTION, "moe_forward_residual: x_next must not alias r_in or r_out");
+  if (res->r_out == x || (const uint16_t*)res->r_in == x)
+    return fail(MOE_ERR_OPTION, "moe_forward_residual: x must not alias r_in or r_out");
+  return forward_impl("moe_forward_residual", d, opts, x, router, experts, shared, nullptr, res,
+                      routing_out, ws, ws_bytes, stream);
+}
+
+size_t moe_dense_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t S) {
+  if (check_dense(T, H, I, S) != MOE_OK) return 0;
+  smoe::Plan p;
+  smoe::make_plan(T, H, S, S, I / S, 0, &p);
+  return p.ws_total;
+}
+
+moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint16_t* x,
+                         const moe_ffn* ffn, float swiglu_limit, uint16_t* y, void* ws,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (!x || !ffn || !ffn->w_gate || !ffn->w_up || !ffn->w_down || !y || !ws)
+    return fail(MOE_ERR_NULL, "moe_dense_ffn: NULL argument (x, ffn, ffn->w_*, y, ws)");
+  moe_status st;
+  if ((st = check_dense(T, H, I, S))) return st;
+  if (!isfinite(swiglu_limit) || swiglu_limit < 0.f)
+    return fail(MOE_ERR_OPTION, "moe_dense_ffn: swiglu_limit must be finite and >= 0");
+  if (misaligned(x) || misaligned(ffn->w_gate) || misaligned(ffn->w_up) ||
+      misaligned(ffn->w_down) || misaligned(y) || misaligned(ws))
+    return fail(MOE_ERR_ALIGN, "moe_dense_ffn: device pointers must be 16-byte aligned");
+  if (x == y) return fail(MOE_ERR_OPTION, "moe_dense_ffn: x and y must not alias");
+  smoe::Plan p;
+  smoe::make_plan(T, H, S, S, I / S, 0, &p);
+  if (ws_bytes < p.ws_total)
+    return fail(MOE_ERR_WORKSPACE, "moe_dense_ffn: workspace %zu bytes < required %zu", ws_bytes,
+                p.ws_total);
+  char* w = static_cast<char*>(ws);
+  int32_t* slot = reinterpret_cast<int32_t*>(w + p.ws_slot);
+  {
+    StageMark m(MOE_STAGE_DISPATCH, stream);
+    if ((st = launched(smoe::launch_dense_rows(
+                           p, reinterpret_cast<int32_t*>(w + p.ws_row_token),
+                           reinterpret_cast<float*>(w + p.ws_row_w), slot,
+                           reinterpret_cast<smoe::RowBlock*>(w + p.ws_rb),
+                           reinterpret_cast<int32_t*>(w + p.ws_nrb), stream),
+                       "dense_rows")))
+      return st;
+  }
+  moe_opts o = default_opts();
+  o.swiglu_limit = swiglu_limit;
+  uint16_t* ob = reinterpret_cast<uint16_t*>(w + p.ws_o);
+  if ((st = run_experts(p, o, x, ffn->w_gate, ffn->w_up, ffn->w_down, nullptr, w, ob, stream)))
+    return st;
+  StageMark m(MOE_STAGE_COMBINE, stream);
+  if ((st = launched(smoe::launch_combine(p, ob, slot, y, stream), "combine"))) return st;
+  return ok();
+}
+
+moe_status moe_expert_stats(const moe_dims* d, const int32_t* offsets, const uint16_t* h,
+                            float* stats, float* ratios, hipStream_t stream) {
+  if (!d || !offsets || !h || !stats)
+    return fail(MOE_ERR_NULL, "moe_expert_stats: NULL argument (dims, offsets, h, stats)");
+  moe_status st;
+  if ((st = check_shape(d))) return st;
+  if (misaligned(offsets) || misaligned(h) || misaligned(stats) || misaligned(ratios))
+    return fail(MOE_ERR_ALIGN, "moe_expert_stats: device pointers must be 16-byte aligned");
+  if ((st = launched(smoe::launch_expert_stats(d->T, d->E, d->K, d->I, d->Is, offsets, h, stats,
+                                               ratios, stream),
+                     "expert_stats")))
+    return st;
+  return ok();
+}
+
+moe_status moe_pack_weights_strided(const uint16_t* src, uint16_t* dst, int32_t n_mats,
+                                    int32_t rows, int32_t cols, int64_t ld, int64_t mat_stride,
+                                    hipStream_t stream) {
   if (!src || !dst) return fail(MOE_ERR_NULL, "moe_pack_weights: NULL src or dst");
   if (n_mats < 1 || rows < 16 || cols < 32 || rows % 16 || cols % 32)
     return fail(MOE_ERR_SHAPE,
                 "moe_pack_weights: n_mats=%d rows=%d cols=%d (need >= 1, rows %% 16 == 0, "
                 "cols %% 32 == 0)",
                 n_mats, rows, cols);
+  if (ld < cols || ld % 8 || mat_stride < 0 || mat_stride % 8)
+    return fail(MOE_ERR_SHAPE,
+                "moe_pack_weights: ld=%lld must be >= cols=%d, ld and mat_stride=%lld "
+                "multiples of 8 and mat_stride >= 0",
+                (long long)ld, cols, (long long)mat_stride);
   if (misaligned(src) || misaligned(dst))
     return fail(MOE_ERR_ALIGN, "moe_pack_weights: pointers must be 16-byte aligned");
-  const size_t bytes = (size_t)n_mats * rows * cols * 2;
+  const size_t out_bytes = (size_t)n_mats * rows * cols * 2;
+  const size_t in_bytes = ((size_t)(n_mats - 1) * mat_stride + (size_t)(rows - 1) * ld + cols) * 2;
   const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
-  if (a < b + bytes && b < a + bytes)
+  if (a < b + out_bytes && b < a + in_bytes)
     return fail(MOE_ERR_OPTION, "moe_pack_weights: src and dst overlap");
-  moe_status st = launched(smoe::launch_pack(src, dst, n_mats, rows, cols, stream), "pack");
+  moe_status st = launched(
+      smoe::launch_pack(src, dst, n_mats, rows, cols, ld, mat_stride, stream), "pack");
   if (st) return st;
   return ok();
+}
+
+moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, int32_t rows,
+                            int32_t cols, hipStream_t stream) {
+  return moe_pack_weights_strided(src, dst, n_mats, rows, cols, cols, (int64_t)rows * cols,
+                                  stream);
 }
 
 moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events) {

@@ -1,4 +1,5 @@
-// Combine (un-permute) and the residual + RMSNorm glue between chained layers.
+// Combine (un-permute), the residual + RMSNorm glue between chained layers,
+// and the two fused into one pass.
 //
 // Sources: shd-paper.top summary, 方法详解 / 关键设计 (the selected experts'
 // outputs are mixed with the gate weights); hyper.ai summary, 方法 (one
@@ -57,14 +58,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) = out;
 }
 
-// One workgroup per row: r = r_in (+ y_add) rounded to bf16; x_out =
-// bf16(r / sqrt(mean(r^2) + eps) * (1 + gamma)) computed from the stored
-// bf16 r.  The sum of squares is reduced in a fixed order.
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
-    const uint16_t* r_in, const uint16_t* __restrict__ y_add, const float* __restrict__ gamma,
-    float eps, uint16_t* r_out, uint16_t* __restrict__ x_out, int H) {
+// One workgroup per row, the row's H columns in chunks of 8 per thread.
+//   FUSED = false:  r = r_in (+ y_add)
+//   FUSED = true:   r = r_in + (sum_j o[slot_pos[t,j]] + o[KT + t]), the
+//                   combine of the layer folded into the residual add: the
+//                   layer output is summed in fp32 in slot order (shared
+//                   last) and added to r_in before the one rounding to bf16.
+// r is stored to r_out as bf16; then x_out = bf16(r / sqrt(mean(r^2) + eps)
+// * (1 + gamma)) from the stored bf16 r, the sum of squares reduced in a
+// fixed order.  Each element of r_in/r_out is read and written by the same
+// thread, so r_out may alias r_in.
+struct ResidualArgs {
+  const uint16_t* r_in;
+  const uint16_t* y_add;     // FUSED = false; may be null
+  const uint16_t* o;         // FUSED = true: weighted expert rows [rows_total, H]
+  const int32_t* slot_pos;   // FUSED = true: [T, K]
+  const float* gamma;        // [H] or null (gain 1)
+  float eps;
+  uint16_t* r_out;           // may be null when nothing is added
+  uint16_t* x_out;           // may be null (no norm)
+  int H, K, KT, has_shared;
+};
+
+template <bool FUSED>
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
   __shared__ float s_part[4];
   const int t = blockIdx.x;
+  const int H = a.H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float ss = 0.f;
   float v[8][8];  // H <= 16384: at most 8 chunks of 8 columns per thread
@@ -72,18 +92,37 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
   for (int ch = 0; ch < 8; ++ch) {
     const int c = (ch * 256 + threadIdx.x) * 8;
     if (c < H) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(r_in + (size_t)t * H + c);
+      const u32x4 rin = *reinterpret_cast<const u32x4*>(a.r_in + (size_t)t * H + c);
       float f[8];
-      bf16x8_to_f32(a, f);
-      if (y_add) {
-        const u32x4 b = *reinterpret_cast<const u32x4*>(y_add + (size_t)t * H + c);
-        float fb[8];
-        bf16x8_to_f32(b, fb);
+      bf16x8_to_f32(rin, f);
+      bool add = false;
+      float y[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] = 0.f;
+      if (FUSED) {
+        add = true;
+        for (int j = 0; j < a.K; ++j) {
+          const int row = a.slot_pos[(size_t)t * a.K + j];
+          float fo[8];
+          bf16x8_to_f32(*reinterpret_cast<const u32x4*>(a.o + (size_t)row * H + c), fo);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] += fo[i];
+        }
+        if (a.has_shared) {
+          float fo[8];
+          bf16x8_to_f32(*reinterpret_cast<const u32x4*>(a.o + (size_t)(a.KT + t) * H + c), fo);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) y[i] += fo[i];
+        }
+      } else if (a.y_add) {
+        add = true;
+        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(a.y_add + (size_t)t * H + c), y);
+      }
+      if (add) {
         u32x4 pk;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pk[i] = pack2(f[2 * i] + fb[2 * i], f[2 * i + 1] + fb[2 * i + 1]);
-        if (r_out) *reinterpret_cast<u32x4*>(r_out + (size_t)t * H + c) = pk;
+        for (int i = 0; i < 4; ++i) pk[i] = pack2(f[2 * i] + y[2 * i], f[2 * i + 1] + y[2 * i + 1]);
+        if (a.r_out) *reinterpret_cast<u32x4*>(a.r_out + (size_t)t * H + c) = pk;
         bf16x8_to_f32(pk, f);  // continue from the stored bf16 value
       }
 #pragma unroll
@@ -93,13 +132,13 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
       }
     }
   }
-  if (!x_out) return;
+  if (!a.x_out) return;
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
   if (lane == 0) s_part[wave] = ss;
   __syncthreads();
   const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-  const float inv = 1.0f / sqrtf(tot / (float)H + eps);
+  const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
 #pragma unroll
   for (int ch = 0; ch < 8; ++ch) {
     const int c = (ch * 256 + threadIdx.x) * 8;
@@ -108,13 +147,13 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float g0 = 1.f, g1 = 1.f;
-        if (gamma) {
-          g0 += gamma[c + 2 * i];
-          g1 += gamma[c + 2 * i + 1];
+        if (a.gamma) {
+          g0 += a.gamma[c + 2 * i];
+          g1 += a.gamma[c + 2 * i + 1];
         }
         pk[i] = pack2(v[ch][2 * i] * inv * g0, v[ch][2 * i + 1] * inv * g1);
       }
-      *reinterpret_cast<u32x4*>(x_out + (size_t)t * H + c) = pk;
+      *reinterpret_cast<u32x4*>(a.x_out + (size_t)t * H + c) = pk;
     }
   }
 }
@@ -130,8 +169,21 @@ hipError_t launch_combine(const Plan& p, const uint16_t* o, const int32_t* slot_
 hipError_t launch_residual_rmsnorm(int T, int H, const uint16_t* r_in, const uint16_t* y_add,
                                    const float* gamma, float eps, uint16_t* r_out,
                                    uint16_t* x_out, hipStream_t s) {
-  hipLaunchKernelGGL(residual_rmsnorm_kernel, dim3(T), dim3(256), 0, s, r_in, y_add, gamma, eps,
-                     r_out, x_out, H);
+  ResidualArgs a{};
+  a.r_in = r_in; a.y_add = y_add; a.gamma = gamma; a.eps = eps;
+  a.r_out = r_out; a.x_out = x_out; a.H = H;
+  hipLaunchKernelGGL(residual_rmsnorm_kernel<false>, dim3(T), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_residual(const Plan& p, const uint16_t* o, const int32_t* slot_pos,
+                                   const uint16_t* r_in, const float* gamma, float eps,
+                                   uint16_t* r_out, uint16_t* x_out, hipStream_t s) {
+  ResidualArgs a{};
+  a.r_in = r_in; a.o = o; a.slot_pos = slot_pos; a.gamma = gamma; a.eps = eps;
+  a.r_out = r_out; a.x_out = x_out;
+  a.H = p.H; a.K = p.K; a.KT = p.KT; a.has_shared = p.Is > 0 ? 1 : 0;
+  hipLaunchKernelGGL(residual_rmsnorm_kernel<true>, dim3(p.T), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -11,9 +11,12 @@
 
 namespace smoe {
 
-// One thread copies one lane's 16 bytes of one tile.
+// One thread copies one lane's 16 bytes of one tile.  Source matrix m, row
+// i, column j sits at src[m * mat_stride + i * ld + j], so a matrix can also
+// be a column slice of a wider one.
 __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ src,
                                                    uint16_t* __restrict__ dst, int rows, int cols,
+                                                   long long ld, long long mat_stride,
                                                    long long total_lanes) {
   const long long id = (long long)blockIdx.x * 256 + threadIdx.x;
   if (id >= total_lanes) return;
@@ -25,16 +28,16 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint16_t* __restrict__ 
   const long long t_in = tile % tiles_per_mat;
   const int rt = (int)(t_in / ktiles), kt = (int)(t_in % ktiles);
   const int r = l & 15, g = l >> 4;
-  const uint16_t* s = src + (size_t)mat * rows * cols + (size_t)(rt * 16 + r) * cols + kt * 32 + 8 * g;
+  const uint16_t* s = src + mat * mat_stride + (long long)(rt * 16 + r) * ld + kt * 32 + 8 * g;
   *reinterpret_cast<u32x4*>(dst + (size_t)tile * 512 + l * 8) = *reinterpret_cast<const u32x4*>(s);
 }
 
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,
-                       hipStream_t s) {
+                       long long ld, long long mat_stride, hipStream_t s) {
   const long long lanes = (long long)n_mats * (rows / 16) * (cols / 32) * 64;
   const long long blocks = (lanes + 255) / 256;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, rows, cols,
-                     lanes);
+                     ld, mat_stride, lanes);
   return hipGetLastError();
 }
 

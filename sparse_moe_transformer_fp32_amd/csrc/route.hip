@@ -584,4 +584,45 @@ hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
   return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------
+// Row list of a dense gated FFN run through the grouped GEMMs (the dense
+// layers of the model; hyper.ai summary, 方法, and paperlayer.ai summary,
+// §2.2: the first layers use a dense FFN; model card: intermediate_size).
+// The intermediate dimension is cut into S slices, slice s acting as group
+// s: every token t is row s*T + t of group s with weight 1, and slot s of
+// token t points at that row, so the combine adds the S partial outputs of
+// a token in slice order.  Blocks of one slice are consecutive.
+__global__ __launch_bounds__(256) void dense_rows_kernel(int T, int S, int bn, int32_t* row_token,
+                                                         float* row_w, int32_t* slot_pos,
+                                                         RowBlock* rb, int32_t* n_rb) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int per = (T + bn - 1) / bn;   // blocks per slice
+  if (i < S * T) {
+    const int sl = i / T, t = i - sl * T;
+    row_token[i] = t;
+    row_w[i] = 1.0f;
+    slot_pos[(size_t)t * S + sl] = i;
+  }
+  if (i < S * per) {
+    const int sl = i / per, b = i - sl * per;
+    RowBlock blk{};
+    blk.group = sl;
+    blk.row_start = sl * T + b * bn;
+    blk.n_rows = min(bn, T - b * bn);
+    blk.first = sl * per;
+    blk.n_group = per;
+    rb[i] = blk;
+  }
+  if (i == 0) *n_rb = S * per;
+}
+
+hipError_t launch_dense_rows(const Plan& p, int32_t* row_token, float* row_w, int32_t* slot_pos,
+                             RowBlock* rb, int32_t* n_rb, hipStream_t s) {
+  // p.E = p.K = S slices, p.KT = S * T rows
+  const int n = p.KT;
+  hipLaunchKernelGGL(dense_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.T, p.E, p.bn,
+                     row_token, row_w, slot_pos, rb, n_rb);
+  return hipGetLastError();
+}
+
 }  // namespace smoe

@@ -73,6 +73,9 @@ struct RouteLaunch {
 };
 size_t dispatch_lds_bytes(int E);
 hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s);
+// dense FFN cut into p.E = p.K slices: identity row list, weight 1
+hipError_t launch_dense_rows(const Plan& p, int32_t* row_token, float* row_w, int32_t* slot_pos,
+                             RowBlock* rb, int32_t* n_rb, hipStream_t s);
 
 struct GateUpArgs {
   const uint16_t* wg;   // [E, I, H]
@@ -102,12 +105,19 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,
-                       hipStream_t s);
+                       long long ld, long long mat_stride, hipStream_t s);
 
 hipError_t launch_combine(const Plan& p, const uint16_t* o, const int32_t* slot_pos,
                           uint16_t* y, hipStream_t s);
 hipError_t launch_residual_rmsnorm(int T, int H, const uint16_t* r_in, const uint16_t* y_add,
                                    const float* gamma, float eps, uint16_t* r_out,
                                    uint16_t* x_out, hipStream_t s);
+// per-group activation statistics of h, and their max/min-to-median ratios
+hipError_t launch_expert_stats(int T, int E, int K, int I, int Is, const int32_t* offsets,
+                               const uint16_t* h, float* stats, float* ratios, hipStream_t s);
+// combine + residual add (+ the next layer's RMSNorm when x_out != null)
+hipError_t launch_combine_residual(const Plan& p, const uint16_t* o, const int32_t* slot_pos,
+                                   const uint16_t* r_in, const float* gamma, float eps,
+                                   uint16_t* r_out, uint16_t* x_out, hipStream_t s);
 
 }  // namespace smoe

@@ -165,6 +165,39 @@ def make_inputs(wl: Workload, device: str = "cpu", T: Optional[int] = None,
     return Inputs(wl, x, rw, rb, layer_list, router_ws, router_bs)
 
 
+@dataclasses.dataclass(frozen=True)
+class DenseWorkload:
+    """A dense gated FFN of the model's first layers (model card:
+    intermediate_size 11264; 3 dense of 45 layers)."""
+    name: str
+    T: int
+    H: int
+    I: int
+    seed: int
+    w_std: float = 0.02
+    slices: int = 8
+
+
+DENSE_WORKLOADS: Dict[str, DenseWorkload] = {
+    "dense_decode": DenseWorkload("dense_decode", T=16, H=4096, I=11264, seed=6),
+    "dense_prefill": DenseWorkload("dense_prefill", T=4096, H=4096, I=11264, seed=7),
+}
+
+
+def make_dense_inputs(wl: DenseWorkload, device: str = "cpu", T: Optional[int] = None):
+    """x [T,H] bf16 (rows at unit RMS), Wg, Wu [I,H] and Wd [H,I] bf16 from
+    one generator seeded once, drawn in that order."""
+    T = wl.T if T is None else T
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wl.seed)
+    x = _unit_rms_rows(_normal(gen, (T, wl.H), 1.0, dev)).to(torch.bfloat16)
+    wg = _normal(gen, (wl.I, wl.H), wl.w_std, dev).to(torch.bfloat16)
+    wu = _normal(gen, (wl.I, wl.H), wl.w_std, dev).to(torch.bfloat16)
+    wd = _normal(gen, (wl.H, wl.I), wl.w_std, dev).to(torch.bfloat16)
+    return x, wg, wu, wd
+
+
 def random_tiny(seed: int, T: int, H: int, E: int, K: int, I: int, Is: int,
                 bias_std: float = 0.1, w_std: float = 0.2) -> Inputs:
     """Small random fp32 case for property tests (CPU generator)."""

@@ -182,3 +182,84 @@ def test_pack_weights_checks():
     assert f(_vp(A), _vp(1 << 30), 0, 16, 32, None) == B.MOE_ERR_SHAPE
     assert f(_vp(A + 2), _vp(1 << 30), 1, 16, 32, None) == B.MOE_ERR_ALIGN
     assert f(_vp(A), _vp(A + 512), 1, 16, 32, None) == B.MOE_ERR_OPTION   # overlap
+
+
+def _forward_res(res=None, x=A, ws_bytes=None, dims=FLASH):
+    lib = B.load()
+    d = B.dims(*dims)
+    o = B.make_opts()
+    r = B.Router(_vp(A), _vp(A))
+    e = B.Experts(_vp(A), _vp(A), _vp(A))
+    sh = B.Shared(_vp(A), _vp(A), _vp(A))
+    if res is None:
+        res = B.Residual(_vp(3 * A), _vp(4 * A), _vp(5 * A), None, 1e-6)
+    if ws_bytes is None:
+        ws_bytes = B.workspace_bytes(*dims)
+    return lib.moe_forward_residual(ctypes.byref(d), ctypes.byref(o), _vp(x), ctypes.byref(r),
+                                    ctypes.byref(e), ctypes.byref(sh),
+                                    ctypes.byref(res) if res is not False else None, None,
+                                    _vp(6 * A), ws_bytes, None)
+
+
+def test_forward_residual_checks():
+    R = B.Residual
+    assert _forward_res(res=False) == B.MOE_ERR_NULL
+    assert _forward_res(res=R(None, _vp(4 * A), None, None, 1e-6)) == B.MOE_ERR_NULL
+    assert _forward_res(res=R(_vp(3 * A), None, None, None, 1e-6)) == B.MOE_ERR_NULL
+    assert _forward_res(x=0) == B.MOE_ERR_NULL
+    assert _forward_res(res=R(_vp(3 * A), _vp(4 * A), None, None, -1.0)) == B.MOE_ERR_OPTION
+    assert _forward_res(res=R(_vp(3 * A), _vp(4 * A), _vp(4 * A), None, 1e-6)) == B.MOE_ERR_OPTION
+    assert _forward_res(res=R(_vp(3 * A), _vp(4 * A), _vp(3 * A), None, 1e-6)) == B.MOE_ERR_OPTION
+    assert _forward_res(x=3 * A) == B.MOE_ERR_OPTION               # x aliases r_in
+    assert _forward_res(res=R(_vp(3 * A + 2), _vp(4 * A), None, None, 1e-6)) == B.MOE_ERR_ALIGN
+    assert _forward_res(res=R(_vp(3 * A), _vp(4 * A), None, _vp(A + 4), 1e-6)) == B.MOE_ERR_ALIGN
+    assert _forward_res(ws_bytes=100) == B.MOE_ERR_WORKSPACE
+    # r_out may alias r_in and x_next may alias x: only the workspace fails here
+    ok = R(_vp(3 * A), _vp(3 * A), _vp(A), None, 1e-6)
+    assert _forward_res(res=ok, ws_bytes=100) == B.MOE_ERR_WORKSPACE
+
+
+def test_dense_checks():
+    lib = B.load()
+    assert lib.moe_dense_workspace_bytes(16, 4096, 11264, 8) > 0
+    assert lib.moe_dense_workspace_bytes(16, 4096, 11264, 7) == 0       # 11264 % 7
+    assert lib.moe_dense_workspace_bytes(16, 4096, 11264, 32) == 0      # S > 16
+    assert lib.moe_dense_workspace_bytes(16, 4096, 11264 + 32, 8) == 0  # slices not % 64
+    assert lib.moe_dense_workspace_bytes(0, 4096, 11264, 8) == 0
+    need = lib.moe_dense_workspace_bytes(16, 4096, 11264, 8)
+    f = B.Shared(_vp(A), _vp(A), _vp(A))
+
+    def call(T=16, H=4096, I=11264, S=8, x=A, ffn=f, lim=0.0, y=2 * A, ws=3 * A, n=need):
+        return lib.moe_dense_ffn(T, H, I, S, _vp(x), ctypes.byref(ffn) if ffn else None, lim,
+                                 _vp(y), _vp(ws), n, None)
+
+    assert call(x=0) == B.MOE_ERR_NULL
+    assert call(ffn=B.Shared(_vp(A), None, _vp(A))) == B.MOE_ERR_NULL
+    assert call(I=1000) == B.MOE_ERR_SHAPE
+    assert call(H=4000) == B.MOE_ERR_SHAPE
+    assert call(lim=-1.0) == B.MOE_ERR_OPTION
+    assert call(y=A) == B.MOE_ERR_OPTION
+    assert call(x=A + 2) == B.MOE_ERR_ALIGN
+    assert call(n=need - 1) == B.MOE_ERR_WORKSPACE
+
+
+def test_expert_stats_checks():
+    lib = B.load()
+    d = B.dims(*FLASH)
+    f = lib.moe_expert_stats
+    assert f(ctypes.byref(d), None, _vp(A), _vp(A), None, None) == B.MOE_ERR_NULL
+    assert f(ctypes.byref(d), _vp(A), _vp(A), None, None, None) == B.MOE_ERR_NULL
+    bad = B.dims(16, 4096, 288, 9, 1280, 1280)
+    bad.K = 17
+    assert f(ctypes.byref(bad), _vp(A), _vp(A), _vp(A), None, None) == B.MOE_ERR_SHAPE
+    assert f(ctypes.byref(d), _vp(A), _vp(A), _vp(A), _vp(A + 4), None) == B.MOE_ERR_ALIGN
+
+
+def test_pack_weights_strided_checks():
+    lib = B.load()
+    f = lib.moe_pack_weights_strided
+    assert f(_vp(A), _vp(1 << 30), 2, 16, 32, 16, 32, None) == B.MOE_ERR_SHAPE    # ld < cols
+    assert f(_vp(A), _vp(1 << 30), 2, 16, 32, 68, 32, None) == B.MOE_ERR_SHAPE    # ld % 8
+    assert f(_vp(A), _vp(1 << 30), 2, 16, 32, 64, -8, None) == B.MOE_ERR_SHAPE
+    # the source spans (n-1)*stride + (rows-1)*ld + cols elements: overlap found
+    assert f(_vp(A), _vp(A + 2 * (15 * 64 + 64) - 16), 2, 16, 32, 64, 32, None) == B.MOE_ERR_OPTION

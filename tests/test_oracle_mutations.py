@@ -25,6 +25,11 @@ def _pins_pass():
         P.test_rmsnorm_closed_forms,
         P.test_chain_closed_forms,
         P.test_swiglu_limit_closed_forms,
+        P.test_dense_ffn_textbook,
+        P.test_activation_stats_hand_computed,
+        P.test_norm_ratios_hand_computed,
+        lambda: [P.test_expert_stats_brute_force(s) for s in P.TINY_SHAPES],
+        P.test_norm_ratios_closed_forms,
     ]
     for c in checks:
         try:
@@ -139,7 +144,43 @@ def _logits_transposed_router(x, Wr):
     return x @ Wr[::-1].T
 
 
+_orig_hidden = M.swiglu_hidden
+_orig_stats = M.activation_stats
+
+
+def _stats_mean_square_as_norm(h):
+    h = np.asarray(h, np.float64)
+    if h.shape[0] == 0:
+        return np.zeros(4)
+    n = np.mean(h * h, axis=1)
+    return np.array([h.shape[0], n.sum(), np.sum(n * n), n.max()])
+
+
+def _ratios_lower_median(stats):
+    st = np.asarray(stats, np.float64)
+    act = st[:, 0] > 0
+    m = np.sort(st[act, 1] / st[act, 0])
+    med = m[(len(m) - 1) // 2]
+    return np.array([m.max() / med, m.min() / med])
+
+
+def _ratios_include_empty(stats):
+    st = np.asarray(stats, np.float64)
+    m = st[:, 1] / np.maximum(st[:, 0], 1)
+    med = np.median(m)
+    return np.array([m.max() / med, m.min() / med])
+
+
+def _hidden_gate_only(xr, Wg, Wu, limit=0.0):
+    g = np.asarray(xr, np.float64) @ np.asarray(Wg, np.float64).T
+    return g / (1.0 + np.exp(-g))
+
+
 MUTATIONS = {
+    "stats_mean_square_as_norm": ("activation_stats", _stats_mean_square_as_norm),
+    "ratio_lower_median": ("norm_ratios", _ratios_lower_median),
+    "ratio_counts_empty_experts": ("norm_ratios", _ratios_include_empty),
+    "hidden_drops_up_branch": ("swiglu_hidden", _hidden_gate_only),
     "silu_is_sigmoid": ("silu", _silu_as_sigmoid),
     "sigmoid_wrong_sign": ("router_scores", _scores_wrong_sign),
     "bias_dropped": ("selection_keys", _keys_no_bias),

@@ -310,3 +310,77 @@ def test_swiglu_limit_closed_forms():
     assert np.array_equal(y0, y1)
     y2 = oracle.moe_layer(*a, K=2, limit=1e-3, limit_shared=1e-3)
     assert not np.allclose(y0, y2)
+
+
+# Dense FFN of the first layers: the gated form on every token ---------------
+def test_dense_ffn_textbook():
+    rng = np.random.default_rng(21)
+    T, H, I = 3, 6, 9
+    x = rng.normal(size=(T, H))
+    Wg, Wu, Wd = rng.normal(size=(I, H)), rng.normal(size=(I, H)), rng.normal(size=(H, I))
+    y = oracle.dense_ffn(x, Wg, Wu, Wd)
+    for t in range(T):
+        assert _rel(y[t], np.array(textbook_swiglu_row(x[t], Wg, Wu, Wd))) < 1e-13
+    # cutting the intermediate dimension into slices and adding the partial
+    # outputs gives the same result (the slicing the HIP path uses)
+    parts = sum(oracle.dense_ffn(x, Wg[s:s + 3], Wu[s:s + 3], Wd[:, s:s + 3]) for s in (0, 3, 6))
+    assert _rel(parts, y) < 1e-13
+
+
+# Per-expert activation statistics -------------------------------------------
+def test_activation_stats_hand_computed():
+    h = np.array([[3.0, 4.0], [0.0, 0.0], [6.0, 8.0]])
+    assert np.allclose(oracle.activation_stats(h), [3, 15, 125, 10], rtol=0, atol=1e-12)
+    assert np.array_equal(oracle.activation_stats(np.zeros((0, 2))), np.zeros(4))
+
+
+def test_norm_ratios_hand_computed():
+    # mean norms 1, (empty), 2, 4 -> median 2 over the three with rows
+    st = np.array([[2, 2, 0, 1], [0, 0, 0, 0], [1, 2, 0, 2], [4, 16, 0, 4]], float)
+    assert np.allclose(oracle.norm_ratios(st), [2.0, 0.5], rtol=0, atol=1e-15)
+    # even count: means 1, 2, 3, 10 -> median 2.5
+    st = np.array([[1, 1, 0, 1], [1, 2, 0, 2], [1, 3, 0, 3], [1, 10, 0, 10]], float)
+    assert np.allclose(oracle.norm_ratios(st), [4.0, 0.4], rtol=0, atol=1e-15)
+
+
+@pytest.mark.parametrize("shape", TINY_SHAPES)
+def test_expert_stats_brute_force(shape):
+    """Dense over every (token, expert): norms of the SwiGLU activation with
+    the tanh-form sigmoid, masked by the counting top-K of tests/brute.py."""
+    from tests.brute import _sig
+    seed, T, H, E, K, I, Is = shape
+    inp = random_tiny(seed, T, H, E, K, I, Is)
+    x, Wr, b, Wg, Wu, Wd, Wsg, Wsu, Wsd = _args(inp)
+    keys = _sig(x @ Wr.T) + b[None, :]
+    m = brute_mask(keys, K)
+    G = np.einsum("th,eih->tei", x, Wg)
+    U = np.einsum("th,eih->tei", x, Wu)
+    n = np.sqrt(np.einsum("tei,tei->te", G * _sig(G) * U, G * _sig(G) * U))
+    want = np.stack([m.sum(0), (n * m).sum(0), (n * n * m).sum(0), (n * m).max(0)], axis=1)
+    if Is:
+        gs, us = x @ Wsg.T, x @ Wsu.T
+        ns = np.sqrt(((gs * _sig(gs) * us) ** 2).sum(1))
+        want = np.vstack([want, [T, ns.sum(), (ns * ns).sum(), ns.max()]])
+    sel = oracle.select_topk(oracle.selection_keys(oracle.router_scores(
+        oracle.router_logits(x, Wr)), b), K)
+    got = oracle.expert_activation_stats(x, sel, Wg, Wu, Wsg if Is else None,
+                                         Wsu if Is else None, E=E)
+    assert got.shape == want.shape
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-14)
+
+
+def test_norm_ratios_closed_forms():
+    """Identical experts that see the same tokens have equal mean norms (both
+    ratios 1); scaling one expert's up projection by c scales its norms by c."""
+    rng = np.random.default_rng(31)
+    T, H, E, I = 7, 6, 3, 4
+    x = rng.normal(size=(T, H))
+    wg, wu = rng.normal(size=(I, H)), rng.normal(size=(I, H))
+    sel = np.tile(np.arange(E), (T, 1))                  # K = E: every token on every expert
+    Wg = np.stack([wg] * E)
+    st = oracle.expert_activation_stats(x, sel, Wg, np.stack([wu] * E), E=E)
+    assert np.allclose(oracle.norm_ratios(st), [1.0, 1.0], rtol=0, atol=1e-13)
+    st = oracle.expert_activation_stats(x, sel, Wg, np.stack([wu, wu, 3.0 * wu]), E=E)
+    assert np.allclose(oracle.norm_ratios(st), [3.0, 1.0], rtol=0, atol=1e-13)
+    st = oracle.expert_activation_stats(x, sel, Wg, np.stack([0.5 * wu, wu, wu]), E=E)
+    assert np.allclose(oracle.norm_ratios(st), [1.0, 0.5], rtol=0, atol=1e-13)
