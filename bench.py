@@ -63,13 +63,17 @@ class StageTimer:
             self.arrays.append(arr)
 
     def stage_ms(self):
-        """Mean duration (ms) of each stage over the recorded steps."""
+        """Mean duration (ms) of each stage over the recorded steps; 0 for a
+        stage the call does not run (its events were never recorded)."""
         out = []
         for s in range(self.n_stages):
             tot = 0.0
             for arr in self.arrays:
                 ms = ctypes.c_float()
-                assert self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * s], arr[2 * s + 1]) == 0
+                if self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * s], arr[2 * s + 1]) != 0:
+                    self.hip.hipGetLastError()   # leave no error for the next runtime call
+                    tot = 0.0
+                    break
                 tot += ms.value
             out.append(tot / len(self.arrays))
         return out
@@ -251,6 +255,51 @@ def run_layer_bench(wl_name, steps, warmup, device="cuda"):
                 n_layers=nl)
 
 
+def run_dense_bench(name, steps, warmup, device="cuda"):
+    """The model's dense FFN (moe_dense_ffn) on its synthetic workload:
+    tokens/s, bf16 TFLOP/s and algorithmic GB/s of one call."""
+    import torch
+    from sparse_moe_transformer_fp32_amd import binding as B
+    from sparse_moe_transformer_fp32_amd.inputs import DENSE_WORKLOADS, make_dense_inputs
+
+    wl = DENSE_WORKLOADS[name]
+    x, wg, wu, wd = make_dense_inputs(wl, device)
+    ffn = B.DenseFFN(wg, wu, wd, S=wl.slices, T_max=wl.T)
+    y = torch.empty_like(x)
+    for _ in range(warmup):
+        ffn(x, y)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        ffn(x, y)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    hip = _hip()
+    timer = StageTimer(hip, steps, len(B.STAGES))
+    for k in range(steps):
+        B.set_stage_events(timer.arrays[k])
+        ffn(x, y)
+    B.set_stage_events(None)
+    torch.cuda.synchronize()
+    st = dict(zip(B.STAGES, timer.stage_ms()))
+    timer.close()
+    T, H, I = wl.T, wl.H, wl.I
+    flops = 2 * T * 3 * H * I
+    nbytes = 3 * H * I * 2 + 2 * T * H * 2
+    gu_ms, dn_ms = st["gate_up"], st["down"]
+    return {"workload": f"{wl.name}: dense gated FFN, T={T}, H={H}, I={I}, {wl.slices} slices",
+            "tokens_per_s": round(T / (ms * 1e-3), 1), "ms_per_step": round(ms, 4),
+            "bf16_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gate_up_tflops": round(2 * T * 2 * H * I / (gu_ms * 1e-3) / 1e12, 2),
+            "down_tflops": round(2 * T * H * I / (dn_ms * 1e-3) / 1e12, 2),
+            "stage_ms": {k: round(v, 4) for k, v in st.items() if v > 0}}
+
+
 def cpu_baseline(res, max_tokens=16, budget_s=30.0):
     """Time the float64 oracle on the host on up to `max_tokens` tokens of the
     workload (weights copied to host memory first; the timed region is the
@@ -303,12 +352,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "skew", "skew_mild", "long", "tiny"])
+                    choices=["decode", "prefill", "skew", "skew_mild", "long", "tiny",
+                             "dense_decode", "dense_prefill"])
     ap.add_argument("--no-prefill", action="store_true", help="skip the T=4096 side measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the dense-FFN side measurements of the default run")
     ap.add_argument("--summarize-stats", nargs=3, metavar=("CSV", "OUT", "COMMAND"),
                     help="offline: write a short summary of a rocprofv3 kernel_stats.csv")
     ap.add_argument("--write-traffic", nargs="+", metavar="ARG",
@@ -334,6 +386,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}))
+        return
+    if args.workload.startswith("dense"):
+        d = run_dense_bench(args.workload, args.steps, args.warmup)
+        print(json.dumps({
+            "metric": "dense-FFN tokens/s", "value": d["tokens_per_s"], "unit": "tokens/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": d["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": d["workload"]}, "dense": d}), flush=True)
         return
     res = run_layer_bench(args.workload, args.steps, args.warmup)
     wl = res["wl"]
@@ -406,6 +467,10 @@ def main():
             "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
         }
         del pre
+        torch.cuda.empty_cache()
+    if args.workload == "decode" and not args.no_dense:
+        line["dense"] = {n: run_dense_bench(n, max(5, args.steps // 5), 3)
+                         for n in ("dense_decode", "dense_prefill")}
         torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 

@@ -8,41 +8,53 @@
 // raw config field table: moe_intermediate_size 1280, hidden_size 4096,
 // torch_dtype bfloat16.
 //
-// Workgroup tile: 16 packed weight fragments (256 weight rows; for gate/up
-// 128 intermediate columns as gate/up pairs) x one row block of up to 16*NB
-// tokens.  Each of the 4 waves owns 4 fragments and multiplies them with
-// every token fragment of the block, so each weight element is read from
-// HBM once per row block.
+// Matrix cores: v_mfma_f32_32x32x16_bf16.  Lane l holds A row l%32 and B
+// column l%32, k = 8(l/32)..+7 of a 16-wide k chunk; accumulator register j
+// holds row 8(j/4) + 4(l/32) + j%4 of column l%32.
 //
-// Pipeline, one 32-wide k-step per stage.  The token tile of a stage is
-// shared by all waves: it is gathered row by row straight into B-operand lane
-// order in an NS-slot LDS ring by global_load_lds_dwordx4 (lane l's 16 bytes
-// land at tile base + 16 l), so LDS reads are conflict-free ds_read_b128.
-// Each weight fragment is used by one wave only, so weights skip LDS: a
-// packed weight tile is one contiguous kilobyte already in A-operand lane
-// order and goes straight into a 4-slot register ring, NS-1 steps ahead.
-// Token operands are double-buffered in registers (the LDS reads of step k+1
-// overlap the MFMAs of step k).  Token fragments past the block's rows are
-// skipped.
+// Workgroup tile: 256 weight rows x one row block of up to 192 tokens.  Each
+// of the 4 waves owns two 32-row weight fragments and multiplies them with
+// every 32-token fragment of the block (12 accumulator tiles), so each
+// weight element is read from memory once per row block.  For gate/up a
+// weight fragment is 16 gate rows over 16 up rows of the same intermediate
+// columns, so accumulator registers j and j+8 of a lane are the gate and up
+// values of one output and SwiGLU happens in registers.
+//
+// Pipeline, one 64-wide k stage per step:
+//  - Tokens (shared by the 4 waves) are gathered with full-line loads: one
+//    load instruction moves 8 rows x 128 bytes (8 lanes per row) into
+//    registers, and two stages later the wave writes them to a 2-slot LDS
+//    ring, lane l's 16 bytes at row-group base + 16 l.  The global side
+//    fetches chunk (l%8) ^ s(row) of its row, s(row) = (row/2) % 8: the
+//    swizzle spreads the rows of every 8-lane read group over distinct LDS
+//    banks, and ds_read_b128 of a B operand is conflict-free.  (Loads that
+//    write LDS directly are not used: their completion is not ordered with
+//    the register loads of the same wave, so a vmcnt count cannot tell
+//    when their data has landed.)
+//  - Weights are used by one wave only and skip LDS: packed tiles go straight
+//    into a 3-slot register ring.  One 64-wide stage of a packed 16-row tile
+//    is 1024 contiguous elements.
+//  - Stage s issues the weights of stage s+2 and the tokens of stage s+3,
+//    multiplies its four k chunks
+//    (the LDS reads of chunk q+1 in flight under the MFMAs of chunk q), and
+//    before its last chunk stores stage s+1's tokens to LDS and meets the
+//    other waves at a barrier, so the first chunk of stage s+1 is read under
+//    that last chunk's MFMAs.
+//  - The number of 32-token fragments with real rows is a template argument,
+//    so the MFMA stream has no branches.
 //
 // XCD-aware order: block b runs on XCD b % 8; work items are dealt so that
 // each XCD walks a contiguous range of items ordered (group, weight tile,
 // row block).  Workgroups that run side by side on one XCD then share weight
-// tiles (across an expert's row blocks) and token rows (across weight tiles),
-// and since they advance through K at about the same pace, each k-step's
-// tiles are fetched from HBM once and served to the others from L2.
-#include "smoe_internal.h"
-
+// tiles (across an expert's row blocks) and token rows (across weight tiles)
+// through that XCD's L2.
 #include <type_traits>
 
-#ifndef SMOE_LDS_STAGES
-#define SMOE_LDS_STAGES 4
-#endif
+#include "smoe_internal.h"
 
 namespace smoe {
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void glob_void_t;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct LdsGemmParams {
   const uint16_t* wa0;   // gate/up: gate (packed) [E,I,H];  down: down (packed) [E,H,I]
@@ -59,6 +71,17 @@ struct LdsGemmParams {
   float limit, limit_shared;
 };
 
+namespace {
+
+constexpr int kRows = 192;            // token rows per row block (the plan's bn)
+constexpr int kFR = 2;                // 32-row weight fragments per wave
+constexpr int kKC = 4;                // 16-wide k chunks per 64-wide stage
+constexpr int kTL = kRows / 8 / 4;    // token loads per wave per stage (8 rows each)
+constexpr int kLoads = kFR * kKC + kTL;  // vector-memory ops per wave per stage
+constexpr int kStage = kRows * 128;   // token bytes per stage
+constexpr int kWSlots = 3;            // weight register ring slots
+constexpr int kTSlots = 2;            // LDS ring slots (and token staging buffers)
+
 __device__ inline uint32_t pack_bf16x2_l(float a, float b) {
   const __bf16 ha = (__bf16)a, hb = (__bf16)b;
   return (uint32_t)__builtin_bit_cast(uint16_t, ha) |
@@ -73,27 +96,243 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
 }
 
-// s_waitcnt vmcnt(n) lgkmcnt(0): also every LDS read of this wave is done.
-template <int N>
-__device__ inline void wait_vmcnt_lds() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0x0 << 8) | (((N >> 4) & 3) << 14));
+// s_waitcnt lgkmcnt(0): every LDS access of this wave is done.
+__device__ inline void wait_lds() {
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (3 << 14));
 }
 
-template <int MODE, int NB, int NS>
-__global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
-  constexpr int FRW = 4;                  // weight fragments per wave
-  constexpr int NBW = NB / 4;             // token fragments each wave loads
-  static_assert(NB % 4 == 0, "token fragments are loaded 4 ways");
-  constexpr int STAGE = NB * 1024;         // bytes of token tiles per stage
-  constexpr int LOADS = FRW + NBW;        // vector-memory ops per wave per stage
-  static_assert(NS % 2 == 0 && NS >= 4 && NS <= 8, "ring of 4, 6 or 8 slots");
-  static_assert(LOADS * (NS - 1) < 64, "vmcnt range");
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[NS][STAGE];
+// LDS bank swizzle of a token row's 16-byte chunks
+__device__ inline int row_swizzle(int R) { return (R >> 1) & 7; }
 
+template <int I>
+using ic = std::integral_constant<int, I>;
+
+}  // namespace
+
+// The pipelined K loop and the epilogue for one work item whose row block
+// has NA 32-token fragments with real rows.
+template <int MODE, int NA>
+__device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowBlock& blk,
+                                              bool shared, int col0, int nst,
+                                              unsigned char (*ring)[kStage]) {
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int r = lane & 15, g = lane >> 4;
+  const int l31 = lane & 31, hi = lane >> 5;
+  const int ktiles = 2 * nst;   // packed 32-wide tiles along K
+
+  // weights: this lane's row of each 32-row fragment, in the packed 16x32
+  // tiles (element (r, 8g..8g+7) of a tile at 8 (16 g + r)); chunk q of
+  // stage s sits at +1024 s + 256 q from the base below
+  const uint16_t* wsrc[kFR];
+  if (MODE == 0) {
+    const uint16_t* Wg = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.I * P.H;
+    const uint16_t* Wu = shared ? P.sa1 : P.wa1 + (size_t)blk.group * P.I * P.H;
+    const uint16_t* M = (l31 < 16) ? Wg : Wu;   // fragment rows 0-15 gate, 16-31 up
+#pragma unroll
+    for (int f = 0; f < kFR; ++f) {
+      const int rt = (col0 >> 4) + wave * kFR + f;
+      wsrc[f] = M + (size_t)rt * ktiles * 512 + 8 * (lane & 15) + 128 * hi;
+    }
+  } else {
+    const uint16_t* Wd = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.H * P.I;
+#pragma unroll
+    for (int f = 0; f < kFR; ++f) {
+      const int rt = (col0 >> 4) + wave * 2 * kFR + 2 * f + (l31 >> 4);
+      wsrc[f] = Wd + (size_t)rt * ktiles * 512 + 8 * (lane & 15) + 128 * hi;
+    }
+  }
+  // tokens: load i of this wave brings rows 8 g .. 8 g + 7 (g = wave*kTL + i),
+  // 8 lanes per row; rows past the block repeat its last row
+  const uint16_t* tsrc[kTL];
+#pragma unroll
+  for (int i = 0; i < kTL; ++i) {
+    const int R = 8 * (wave * kTL + i) + (lane >> 3);
+    const int row = blk.row_start + min(R, blk.n_rows - 1);
+    const uint16_t* base;
+    if (MODE == 0)
+      base = P.bsrc + (size_t)P.row_token[row] * P.H;
+    else
+      base = shared ? P.bsrc + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
+                    : P.bsrc + (size_t)row * P.I;
+    tsrc[i] = base + 8 * ((lane & 7) ^ row_swizzle(R));
+  }
+  // B operand of fragment n, chunk q: row R = 32 n + l31, 16-byte chunk
+  // 2 q + hi of that row, at (R/8)*1024 + (R%8)*128 + (chunk ^ s(R))*16
+  int roff[kKC];
+#pragma unroll
+  for (int q = 0; q < kKC; ++q)
+    roff[q] = (l31 >> 3) * 1024 + (lane & 7) * 128 + (((2 * q + hi) ^ ((l31 >> 1) & 7)) << 4);
+
+  f32x16 acc[kFR][NA];
+#pragma unroll
+  for (int f = 0; f < kFR; ++f)
+#pragma unroll
+    for (int n = 0; n < NA; ++n)
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[f][n][j] = 0.f;
+
+  // past the end of K every load re-reads the last stage (in bounds; unused)
+  auto load_w = [&](u32x4 (&w)[kFR][kKC], int s) {
+    const size_t off = (size_t)min(s, nst - 1) * 1024;
+#pragma unroll
+    for (int f = 0; f < kFR; ++f)
+#pragma unroll
+      for (int q = 0; q < kKC; ++q)
+        w[f][q] = *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
+  };
+  auto load_t = [&](u32x4 (&v)[kTL], int s) {
+    const int off = min(s, nst - 1) * 64;
+#pragma unroll
+    for (int i = 0; i < kTL; ++i) v[i] = *reinterpret_cast<const u32x4*>(tsrc[i] + off);
+  };
+  auto write_t = [&](unsigned char* slot, const u32x4 (&v)[kTL]) {
+#pragma unroll
+    for (int i = 0; i < kTL; ++i)
+      *reinterpret_cast<u32x4*>(slot + (wave * kTL + i) * 1024 + lane * 16) = v[i];
+  };
+  auto read_t = [&](const unsigned char* slot, int q, u32x4 (&t)[NA]) {
+#pragma unroll
+    for (int n = 0; n < NA; ++n)
+      t[n] = *reinterpret_cast<const u32x4*>(slot + n * 4096 + roff[q]);
+  };
+  auto mma = [&](const u32x4 (&w)[kFR][kKC], int q, const u32x4 (&t)[NA]) {
+#pragma unroll
+    for (int n = 0; n < NA; ++n)
+#pragma unroll
+      for (int f = 0; f < kFR; ++f)
+        acc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, w[f][q]), __builtin_bit_cast(bf16x8, t[n]), acc[f][n], 0,
+            0, 0);
+  };
+
+  u32x4 w[kWSlots][kFR][kKC];   // weights of stages s, s+1, s+2
+  u32x4 ts[3][kTL];              // tokens of stages s+1..s+3 on their way to LDS
+  u32x4 t[2][NA];                // B operands of the current and the next k chunk
+  // Stage s (weight slot s%3, token staging buffer s%3, LDS slot s%2) first
+  // issues the weights of stage s+2 and the tokens of stage s+3.  Stage s+1's
+  // tokens were loaded two stages ago; all loads go to registers and
+  // complete in order, so vmcnt(2*kLoads) leaves only the two younger
+  // stages' loads in flight and they have arrived.  They go to LDS slot
+  // (s+1)%2, last read in stage s-1 (every wave finished those reads before
+  // the barrier of stage s-1, which all waves have passed).  The barrier
+  // after lgkmcnt(0) publishes them for the first chunk of s+1.
+  auto stage = [&](auto wc, auto sc, auto tc, int s) {
+    constexpr int jw = decltype(wc)::value;   // s % 3
+    constexpr int js = decltype(sc)::value;   // s % 3 (staging buffer of stage s+3)
+    constexpr int jt = decltype(tc)::value;   // s % 2
+    constexpr int jw2 = (jw + 2) % kWSlots, js1 = (js + 1) % 3, jt1 = (jt + 1) % kTSlots;
+    load_w(w[jw2], s + 2);
+    load_t(ts[js], s + 3);
+    __builtin_amdgcn_sched_barrier(0);
+    read_t(ring[jt], 1, t[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(w[jw], 0, t[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_t(ring[jt], 2, t[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(w[jw], 1, t[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_t(ring[jt], 3, t[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(w[jw], 2, t[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<2 * kLoads>();
+    write_t(ring[jt1], ts[js1]);
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_t(ring[jt1], 0, t[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(w[jw], 3, t[1]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // prologue in the same issue pattern: T0, then (W0, T1) and (W1, T2) as
+  // stages -2 and -1 would issue them
+  load_t(ts[0], 0);
+  load_w(w[0], 0);
+  load_t(ts[1], 1);
+  load_w(w[1], 1);
+  load_t(ts[2], 2);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<2 * kLoads>();   // stage 0's tokens have arrived
+  write_t(ring[0], ts[0]);
+  wait_lds();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read_t(ring[0], 0, t[0]);
+  // stage s stages tokens of s+3 in buffer s%3 (buffer (s+3)%3 = s%3)
+  int s = 0;
+  for (; s + 6 <= nst; s += 6) {
+    stage(ic<0>{}, ic<0>{}, ic<0>{}, s);
+    stage(ic<1>{}, ic<1>{}, ic<1>{}, s + 1);
+    stage(ic<2>{}, ic<2>{}, ic<0>{}, s + 2);
+    stage(ic<0>{}, ic<0>{}, ic<1>{}, s + 3);
+    stage(ic<1>{}, ic<1>{}, ic<0>{}, s + 4);
+    stage(ic<2>{}, ic<2>{}, ic<1>{}, s + 5);
+  }
+  // tail: the remaining stages continue the same slot sequence
+  if (s < nst) stage(ic<0>{}, ic<0>{}, ic<0>{}, s);
+  if (s + 1 < nst) stage(ic<1>{}, ic<1>{}, ic<1>{}, s + 1);
+  if (s + 2 < nst) stage(ic<2>{}, ic<2>{}, ic<0>{}, s + 2);
+  if (s + 3 < nst) stage(ic<0>{}, ic<0>{}, ic<1>{}, s + 3);
+  if (s + 4 < nst) stage(ic<1>{}, ic<1>{}, ic<0>{}, s + 4);
+  wait_vmcnt<0>();
+
+  // epilogue: accumulator register j of a lane is weight row
+  // 8(j/4) + 4 hi + j%4 of the fragment, token row 32 n + l31
+#pragma unroll
+  for (int n = 0; n < NA; ++n) {
+    const int R = 32 * n + l31;
+    if (R >= blk.n_rows) continue;
+    const int row = blk.row_start + R;
+    if (MODE == 0) {
+      const float lim = shared ? P.limit_shared : P.limit;
+      uint16_t* hrow = shared ? P.out + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
+                              : P.out + (size_t)row * P.I;
+#pragma unroll
+      for (int f = 0; f < kFR; ++f) {
+        const int cb = col0 + wave * 16 * kFR + 16 * f;   // first column of fragment f
+        float hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float gv = acc[f][n][j];
+          float uv = acc[f][n][j + 8];
+          if (lim > 0.f) {
+            gv = fminf(gv, lim);
+            uv = fminf(fmaxf(uv, -lim), lim);
+          }
+          hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+        }
+        u32x2 p0, p1;
+        p0[0] = pack_bf16x2_l(hv[0], hv[1]);
+        p0[1] = pack_bf16x2_l(hv[2], hv[3]);
+        p1[0] = pack_bf16x2_l(hv[4], hv[5]);
+        p1[1] = pack_bf16x2_l(hv[6], hv[7]);
+        *reinterpret_cast<u32x2*>(hrow + cb + 4 * hi) = p0;
+        *reinterpret_cast<u32x2*>(hrow + cb + 8 + 4 * hi) = p1;
+      }
+    } else {
+      const float wr = P.row_w[row];
+      uint16_t* orow = P.out + (size_t)row * P.H;
+#pragma unroll
+      for (int f = 0; f < kFR; ++f) {
+        const int rb0 = col0 + wave * 32 * kFR + 32 * f;   // first output row of fragment f
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          u32x2 pk;
+          pk[0] = pack_bf16x2_l(acc[f][n][4 * jj] * wr, acc[f][n][4 * jj + 1] * wr);
+          pk[1] = pack_bf16x2_l(acc[f][n][4 * jj + 2] * wr, acc[f][n][4 * jj + 3] * wr);
+          *reinterpret_cast<u32x2*>(orow + rb0 + 8 * jj + 4 * hi) = pk;
+        }
+      }
+    }
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kTSlots][kStage];
 
   // XCD-aware deal of work items; items run in (group, weight tile, row
   // block) order, so the row blocks that share a weight tile and the tiles
@@ -116,185 +355,14 @@ __global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
   const int nout = (MODE == 0) ? inter : P.H;
   const int col0 = tile * (MODE == 0 ? 128 : 256);  // first output column of the workgroup
   if (col0 >= nout) return;                          // uniform over the workgroup
-  const int Kdim = (MODE == 0) ? P.H : inter;
-  const int nsteps = Kdim >> 5;
-  const int nb_act = (blk.n_rows + 15) >> 4;         // token fragments with real rows
-
-  // this wave's weight fragments (packed, row-tile-major)
-  const uint16_t* wsrc[FRW];
-  if (MODE == 0) {
-    const uint16_t* Wg = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.I * P.H;
-    const uint16_t* Wu = shared ? P.sa1 : P.wa1 + (size_t)blk.group * P.I * P.H;
-#pragma unroll
-    for (int f = 0; f < FRW; ++f) {
-      const int rt = (col0 >> 4) + wave * 2 + (f >> 1);
-      wsrc[f] = ((f & 1) ? Wu : Wg) + (size_t)rt * nsteps * 512 + lane * 8;
-    }
-  } else {
-    const uint16_t* Wd = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.H * P.I;
-#pragma unroll
-    for (int f = 0; f < FRW; ++f) {
-      const int rt = (col0 >> 4) + wave * FRW + f;
-      wsrc[f] = Wd + (size_t)rt * nsteps * 512 + lane * 8;
-    }
-  }
-  // token fragments this wave loads: nb = wave*NBW + i; rows past the block
-  // repeat its last row
-  const uint16_t* tsrc[NBW];
-#pragma unroll
-  for (int i = 0; i < NBW; ++i) {
-    const int nb = wave * NBW + i;
-    const int row = blk.row_start + min(nb * 16 + r, blk.n_rows - 1);
-    const uint16_t* base;
-    if (MODE == 0)
-      base = P.bsrc + (size_t)P.row_token[row] * P.H;
-    else
-      base = shared ? P.bsrc + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
-                    : P.bsrc + (size_t)row * P.I;
-    tsrc[i] = base + 8 * g;
-  }
-
-  f32x4 acc[FRW][NB];
-#pragma unroll
-  for (int f = 0; f < FRW; ++f)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[f][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // past the end of K every load re-reads the last step (harmless, in bounds)
-  auto load_w = [&](u32x4 (&a)[FRW], int step) {
-    const int ks = min(step, nsteps - 1);
-#pragma unroll
-    for (int f = 0; f < FRW; ++f)
-      a[f] = *reinterpret_cast<const u32x4*>(wsrc[f] + (size_t)ks * 512);
-  };
-  auto load_t = [&](unsigned char* st, int step) {
-    const int ks = min(step, nsteps - 1);
-#pragma unroll
-    for (int i = 0; i < NBW; ++i)
-      __builtin_amdgcn_global_load_lds((glob_void_t*)(tsrc[i] + ks * 32),
-                                       (lds_void_t*)(st + (wave * NBW + i) * 1024), 16, 0, 0);
-  };
-  auto read_t = [&](const unsigned char* st, u32x4 (&b)[NB]) {
-    // fragments past the block hold valid repeated rows; their MFMAs are skipped
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-      b[nb] = *reinterpret_cast<const u32x4*>(st + nb * 1024 + lane * 16);
-  };
-  auto mma = [&](const u32x4 (&a)[FRW], const u32x4 (&b)[NB]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      if (nb < nb_act) {
-#pragma unroll
-        for (int f = 0; f < FRW; ++f)
-          acc[f][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, a[f]), __builtin_bit_cast(bf16x8, b[nb]), acc[f][nb],
-              0, 0, 0);
-      }
-    }
-  };
-  // One k-step (j = k mod NS, a compile-time slot index).  Step k issues the
-  // weights of step k+NS-1 and the tokens of step k+NS.  The tokens of step
-  // k+1 were issued NS-1 steps ago, so exactly NS-2 steps' ops are younger:
-  // the wait below completes the weights of step k and the tokens of step
-  // k+1 (and, lgkmcnt(0), this wave's LDS reads of step k).  The barrier then
-  // makes everyone's token tile k+1 visible and frees slot j for step k+NS.
-  u32x4 w[NS][FRW];
-  u32x4 t[2][NB];
-  auto step = [&](auto jc, int k) {
-    constexpr int j = decltype(jc)::value;
-    wait_vmcnt_lds<LOADS * (NS - 2)>();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);  // this step's loads stay after the wait
-    load_w(w[(j + NS - 1) % NS], k + NS - 1);
-    load_t(ring[j], k + NS);
-    read_t(ring[(j + 1) % NS], t[(j + 1) % 2]);
-    __builtin_amdgcn_sched_barrier(0);  // the loads go out before the MFMAs
-    mma(w[j], t[j % 2]);
-  };
-
-  // prologue, issued in this exact order (scheduling barriers keep the
-  // compiler from interleaving the groups): T0 W0 T1 W1 ... T(NS-2) W(NS-2) T(NS-1)
-#pragma unroll
-  for (int s2 = 0; s2 < NS - 1; ++s2) {
-    load_t(ring[s2], s2);
-    load_w(w[s2], s2);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  load_t(ring[NS - 1], NS - 1);
-  __builtin_amdgcn_sched_barrier(0);
-  // T0 and W0 are the LOADS oldest ops: wait until the rest remain
-  wait_vmcnt_lds<LOADS * (NS - 2) + NBW>();
-  __builtin_amdgcn_s_barrier();
-  read_t(ring[0], t[0]);
-  int k = 0;
-  for (; k + NS <= nsteps; k += NS) {
-    step(std::integral_constant<int, 0>{}, k);
-    step(std::integral_constant<int, 1>{}, k + 1);
-    step(std::integral_constant<int, 2>{}, k + 2);
-    step(std::integral_constant<int, 3>{}, k + 3);
-    if constexpr (NS > 4) {
-      step(std::integral_constant<int, 4 % NS>{}, k + 4);
-      step(std::integral_constant<int, 5 % NS>{}, k + 5);
-    }
-    if constexpr (NS > 6) {
-      step(std::integral_constant<int, 6 % NS>{}, k + 6);
-      step(std::integral_constant<int, 7 % NS>{}, k + 7);
-    }
-  }
-  // tail: the remaining steps continue the same slot sequence
-  if (k < nsteps) step(std::integral_constant<int, 0>{}, k);
-  if (k + 1 < nsteps) step(std::integral_constant<int, 1>{}, k + 1);
-  if (k + 2 < nsteps) step(std::integral_constant<int, 2>{}, k + 2);
-  if constexpr (NS > 4) {
-    if (k + 3 < nsteps) step(std::integral_constant<int, 3>{}, k + 3);
-    if (k + 4 < nsteps) step(std::integral_constant<int, 4 % NS>{}, k + 4);
-  }
-  if constexpr (NS > 6) {
-    if (k + 5 < nsteps) step(std::integral_constant<int, 5 % NS>{}, k + 5);
-    if (k + 6 < nsteps) step(std::integral_constant<int, 6 % NS>{}, k + 6);
-  }
-  wait_vmcnt<0>();  // no LDS write may be in flight when the workgroup ends
-
-  // epilogue: lane holds output columns (frag base) + 4g..4g+3 of token row r
-  const int cw = col0 + wave * (MODE == 0 ? 32 : 64);   // this wave's first column
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int lr = nb * 16 + r;
-    if (nb >= nb_act || lr >= blk.n_rows) continue;
-    const int row = blk.row_start + lr;
-    if (MODE == 0) {
-      const float lim = shared ? P.limit_shared : P.limit;
-      uint16_t* hrow = shared ? P.out + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
-                              : P.out + (size_t)row * P.I;
-#pragma unroll
-      for (int pf = 0; pf < FRW / 2; ++pf) {
-        float hv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float gv = acc[2 * pf][nb][j];
-          float uv = acc[2 * pf + 1][nb][j];
-          if (lim > 0.f) {
-            gv = fminf(gv, lim);
-            uv = fminf(fmaxf(uv, -lim), lim);
-          }
-          hv[j] = gv / (1.0f + __expf(-gv)) * uv;
-        }
-        u32x2 pk;
-        pk[0] = pack_bf16x2_l(hv[0], hv[1]);
-        pk[1] = pack_bf16x2_l(hv[2], hv[3]);
-        *reinterpret_cast<u32x2*>(hrow + cw + pf * 16 + 4 * g) = pk;
-      }
-    } else {
-      const float w = P.row_w[row];
-      uint16_t* orow = P.out + (size_t)row * P.H;
-#pragma unroll
-      for (int f = 0; f < FRW; ++f) {
-        u32x2 pk;
-        pk[0] = pack_bf16x2_l(acc[f][nb][0] * w, acc[f][nb][1] * w);
-        pk[1] = pack_bf16x2_l(acc[f][nb][2] * w, acc[f][nb][3] * w);
-        *reinterpret_cast<u32x2*>(orow + cw + f * 16 + 4 * g) = pk;
-      }
-    }
+  const int nst = ((MODE == 0) ? P.H : inter) >> 6;  // 64-wide k stages
+  switch ((blk.n_rows + 31) >> 5) {                   // 32-token fragments with rows
+    case 1: lds_gemm_item<MODE, 1>(P, blk, shared, col0, nst, ring); break;
+    case 2: lds_gemm_item<MODE, 2>(P, blk, shared, col0, nst, ring); break;
+    case 3: lds_gemm_item<MODE, 3>(P, blk, shared, col0, nst, ring); break;
+    case 4: lds_gemm_item<MODE, 4>(P, blk, shared, col0, nst, ring); break;
+    case 5: lds_gemm_item<MODE, 5>(P, blk, shared, col0, nst, ring); break;
+    default: lds_gemm_item<MODE, 6>(P, blk, shared, col0, nst, ring); break;
   }
 }
 
@@ -306,23 +374,25 @@ static unsigned lds_grid(const Plan& p, int tiles) {
 }
 
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s) {
+  if (p.bn != kRows || p.H % 64 || p.I % 128 || p.Is % 128) return hipErrorInvalidValue;
   LdsGemmParams gp{};
   gp.wa0 = a.wg; gp.wa1 = a.wu; gp.sa0 = a.sg; gp.sa1 = a.su; gp.bsrc = a.x;
   gp.row_token = a.row_token; gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.h;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.gu_tiles;
   gp.limit = a.limit; gp.limit_shared = a.limit_shared;
-  hipLaunchKernelGGL((expert_gemm_lds_kernel<0, 12, SMOE_LDS_STAGES>), dim3(lds_grid(p, p.gu_tiles)), dim3(256),
-                     0, s, gp);
+  hipLaunchKernelGGL(expert_gemm_lds_kernel<0>, dim3(lds_grid(p, p.gu_tiles)), dim3(256), 0, s,
+                     gp);
   return hipGetLastError();
 }
 
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
+  if (p.bn != kRows || p.H % 256 || p.I % 128 || p.Is % 128) return hipErrorInvalidValue;
   LdsGemmParams gp{};
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
   gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.o;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.dn_tiles;
-  hipLaunchKernelGGL((expert_gemm_lds_kernel<1, 12, SMOE_LDS_STAGES>), dim3(lds_grid(p, p.dn_tiles)), dim3(256),
-                     0, s, gp);
+  hipLaunchKernelGGL(expert_gemm_lds_kernel<1>, dim3(lds_grid(p, p.dn_tiles)), dim3(256), 0, s,
+                     gp);
   return hipGetLastError();
 }
 
