@@ -138,6 +138,12 @@ def summarize_stats(csv_path, out_path, command, regex="smoe"):
     print("\n".join(lines))
 
 
+# the gate/up kernel each counter workload launches (decode: register-streaming;
+# prefill: LDS-pipelined)
+GATE_UP_KERNEL = {"decode": "void smoe::expert_gemm_kernel<0,",
+                  "prefill": "void smoe::expert_gemm_lds_kernel<0>"}
+
+
 def write_traffic(pmc_root, commands):
     """From rocprofv3 --pmc runs laid out as <pmc_root>/<name>_<COUNTER>/
     run_counter_collection.csv for name in copy/decode/prefill, compute the
@@ -166,7 +172,7 @@ def write_traffic(pmc_root, commands):
             b = fe[k] * 1024 * f_fetch + wr.get(k, 0.0) * 1024 * f_write
             text.append(f"{wl:8s} fetch {fe[k] * 1024 * f_fetch / 1e9:9.4f} GB  write "
                         f"{wr.get(k, 0.0) * 1024 * f_write / 1e9:9.4f} GB  {k}")
-            if "expert_gemm" in k and ("<0," in k):   # gate/up + SwiGLU
+            if k.startswith(GATE_UP_KERNEL[wl]):   # gate/up + SwiGLU of this workload
                 out[f"gate_up:{wl}"] = {"kernel": k, "bytes_per_launch": int(b),
                                         "fetch_kib": fe[k], "write_kib": wr.get(k, 0.0),
                                         "fetch_factor": f_fetch, "write_factor": f_write,
