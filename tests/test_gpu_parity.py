@@ -478,3 +478,50 @@ def test_expert_stats_blow_up_shows_in_ratio():
 def test_expert_stats_flash_decode():
     g, _ = _flash("decode")
     _stats_case(g, 8)
+
+
+# ---------------------------------------------------------------- per-kernel intermediates
+@pytest.mark.parametrize("name", ["ragged_nb1_ksplit2", "nb2", "lds_block", "lds_I_ne_Is"])
+def test_gate_up_and_down_intermediates(name):
+    """The two grouped GEMMs on their own: h (SwiGLU output, expert-contiguous
+    rows, then the shared rows) and o (each row already times its routing
+    weight) read from the workspace, against the oracle's per-row values for
+    the GPU's own routing."""
+    seed, T, H, E, K, I, Is = SMALL[name]
+    g = _small(seed, T, H, E, K, I, Is)
+    layer = B.MoELayer(g["Wr"], g["b"], g["wg"], g["wu"], g["wd"], g["sg"], g["su"], g["sd"], K=K)
+    rt = B.alloc_routing(T, E, K, DEV)
+    layer.forward(g["x"], routing=rt)
+    torch.cuda.synchronize()
+    lay = B.workspace_layout(T, H, E, K, I, Is)
+    ws = layer.workspace()
+    KT = T * K
+    h = host_f64(ws[lay.h:lay.h + (KT * I + T * Is) * 2].view(torch.bfloat16))
+    rows = KT + (T if Is else 0)
+    o = host_f64(ws[lay.o:lay.o + rows * H * 2].view(torch.bfloat16)).reshape(rows, H)
+    f = {k: (None if v is None else host_f64(v)) for k, v in g.items()}
+    perm = rt["perm_token"].cpu().numpy()
+    off = rt["offsets"].cpu().numpy()
+    sel = rt["topk_idx"].cpu().numpy()
+    w = rt["topk_w"].cpu().numpy().astype(np.float64)
+    slot = rt["slot_pos"].cpu().numpy()
+    h_ref = np.zeros((KT, I))
+    o_ref = np.zeros((KT, H))
+    for e in range(E):
+        r = np.arange(off[e], off[e + 1])
+        if r.size == 0:
+            continue
+        oe, he = oracle.swiglu_ffn(f["x"][perm[r]], f["wg"][e], f["wu"][e], f["wd"][e],
+                                   return_hidden=True)
+        h_ref[r], o_ref[r] = he, oe
+    # weight of each routed row: the slot that points at it
+    row_w = np.zeros(KT)
+    row_w[slot.reshape(-1)] = w.reshape(-1)
+    o_ref *= row_w[:, None]
+    check_output(h[:KT * I].reshape(KT, I), h_ref, f"{name} h routed")
+    check_output(o[:KT], o_ref, f"{name} o routed")
+    if Is:
+        os_, hs = oracle.swiglu_ffn(f["x"], f["sg"], f["su"], f["sd"], return_hidden=True)
+        check_output(h[KT * I:].reshape(T, Is), hs, f"{name} h shared")
+        check_output(o[KT:], os_, f"{name} o shared")
+    assert np.array_equal(np.sort(perm[off[0]:off[E]]), np.sort(np.repeat(np.arange(T), K)))
