@@ -255,10 +255,27 @@ def run_layer_bench(wl_name, steps, warmup, device="cuda"):
     inst_ms = (time.perf_counter() - t1) * 1e3 / steps
     stage_ms = timer.stage_ms()
     timer.close()
+    # timed region 3: the same step captured once in a HIP graph and
+    # replayed K times (the library allocates, clears and syncs nothing)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t2 = time.perf_counter()
+    g0.record()
+    for _ in range(steps):
+        graph.replay()
+    g1.record()
+    torch.cuda.synchronize()
+    graph_wall_ms = (time.perf_counter() - t2) * 1e3 / steps
+    graph_ms = g0.elapsed_time(g1) / steps
+    del graph
     counts = routing["counts"].cpu().numpy()
     return dict(wl=wl, inp=inp, layers=layers, routing=routing, counts=counts, wall_ms=wall_ms,
                 gpu_ms=gpu_ms, inst_ms=inst_ms, stage_ms=dict(zip(B.STAGES, stage_ms)),
-                n_layers=nl)
+                n_layers=nl, graph_ms=graph_ms, graph_wall_ms=graph_wall_ms)
 
 
 def run_dense_bench(name, steps, warmup, device="cuda"):
@@ -440,6 +457,7 @@ def main():
         "roofline": rf,
         "layer": {
             "gpu_ms_per_step": round(res["gpu_ms"], 4),
+            "graph_replay_ms_per_step": round(res["graph_ms"], 4),
             "ms_per_step_with_stage_events": round(res["inst_ms"], 4),
             "active_experts": work["n_active"],
             "algorithmic_bytes": work["layer_bytes"],

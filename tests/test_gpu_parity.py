@@ -525,3 +525,45 @@ def test_gate_up_and_down_intermediates(name):
         check_output(h[KT * I:].reshape(T, Is), hs, f"{name} h shared")
         check_output(o[KT:], os_, f"{name} o shared")
     assert np.array_equal(np.sort(perm[off[0]:off[E]]), np.sort(np.repeat(np.arange(T), K)))
+
+
+# ---------------------------------------------------------------- HIP graph capture
+@pytest.mark.parametrize("name", ["ragged_nb1_ksplit2", "lds_block"])
+def test_hip_graph_capture_replays_bitwise(name):
+    """The layer allocates, synchronises and clears nothing, so one call can be
+    captured in a HIP graph.  Three replays, with eager calls on other data
+    in between, each reproduce the eager result bit for bit (output and
+    routing); the fused residual entry point is captured in the same graph."""
+    seed, T, H, E, K, I, Is = SMALL[name]
+    g = _small(seed, T, H, E, K, I, Is)
+    layer = B.MoELayer(g["Wr"], g["b"], g["wg"], g["wu"], g["wd"], g["sg"], g["su"], g["sd"], K=K,
+                       T_max=T)
+    x = g["x"]
+    y = torch.empty_like(x)
+    rt = B.alloc_routing(T, E, K, DEV)
+    r_in = (torch.randn(T, H, generator=torch.Generator().manual_seed(seed)) * 0.5).to(
+        torch.bfloat16).to(DEV)
+    r_out = torch.empty_like(r_in)
+    xn = torch.empty_like(r_in)
+    layer.forward(x, y, rt)
+    layer.forward_residual(x, r_in, r_out, xn)
+    torch.cuda.synchronize()
+    want = (y.clone(), {k: v.clone() for k, v in rt.items()}, r_out.clone(), xn.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layer.forward(x, y, rt)
+        layer.forward_residual(x, r_in, r_out, xn)
+    x_other = torch.randn(T, H, generator=torch.Generator().manual_seed(seed + 1)).to(
+        torch.bfloat16).to(DEV)
+    y_other = torch.empty_like(x)
+    for rep in range(3):
+        for t_ in (y, r_out, xn, *rt.values()):
+            t_.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want[0]), f"replay {rep}: y"
+        for k in rt:
+            assert torch.equal(rt[k], want[1][k]), f"replay {rep}: {k}"
+        assert torch.equal(r_out, want[2]) and torch.equal(xn, want[3]), f"replay {rep}: residual"
+        layer.forward(x_other, y_other)     # eager work between replays
+        torch.cuda.synchronize()
