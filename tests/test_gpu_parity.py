@@ -173,11 +173,11 @@ def test_flash_decode_full():
 
 
 def test_flash_prefill_sampled():
-    _flash_check("prefill", n_sample=24)
+    _flash_check("prefill", n_sample=512)
 
 
 def test_flash_skew_sampled():
-    rg = _flash_check("skew", n_sample=16)
+    rg = _flash_check("skew", n_sample=512)
     from sparse_moe_transformer_fp32_amd.inputs import boosted_experts
     boost = boosted_experts(WORKLOADS["skew"])
     share = rg["counts"][boost].sum() / rg["counts"].sum()
@@ -186,7 +186,7 @@ def test_flash_skew_sampled():
 
 
 def test_flash_skew_mild_sampled():
-    rg = _flash_check("skew_mild", n_sample=16)
+    rg = _flash_check("skew_mild", n_sample=512)
     from sparse_moe_transformer_fp32_amd.inputs import boosted_experts
     boost = boosted_experts(WORKLOADS["skew_mild"])
     share = rg["counts"][boost].sum() / rg["counts"].sum()
@@ -272,8 +272,8 @@ def test_flash_long_chain_teacher_forced_sampled():
     torch.cuda.synchronize()
     rng = np.random.default_rng(5)
     T = wl.T
-    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 14, replace=False)]))
-    route_rows = np.unique(np.concatenate([rows, rng.choice(T, 242, replace=False)]))
+    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 510, replace=False)]))
+    route_rows = np.unique(np.concatenate([rows, rng.choice(T, 1024, replace=False)]))
     for li, (r_l, x_l, rt) in enumerate(trace):
         print(f"layer {li}", flush=True)
         L = inp.layers[li]
