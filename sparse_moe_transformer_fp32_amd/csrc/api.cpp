@@ -202,6 +202,8 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
   if (nb == 12 && !(I % 128 == 0 && Is % 128 == 0 && H % 256 == 0)) nb = 4;
   p->nb = nb;
   p->bn = 16 * nb;
+  // the LDS kernels multiply 32-token fragments, the register kernels 16
+  p->rb_gran = nb == 12 ? 32 : 16;
   p->rb_max = std::min(E, p->KT) + p->KT / p->bn + (Is > 0 ? (T + p->bn - 1) / p->bn : 0);
   if (nb == 1) {
     p->ksplit_gu = 4;

@@ -40,14 +40,16 @@
 //    before its last chunk stores stage s+1's tokens to LDS and meets the
 //    other waves at a barrier, so the first chunk of stage s+1 is read under
 //    that last chunk's MFMAs.
-//  - The number of 32-token fragments with real rows is a template argument,
-//    so the MFMA stream has no branches.
+//  - The number of 32-token fragments with real rows (NA) is a template
+//    argument, so the MFMA stream has no branches, and the waves gather only
+//    those fragments' rows (NA loads per wave per stage).
 //
-// XCD-aware order: block b runs on XCD b % 8; work items are dealt so that
-// each XCD walks a contiguous range of items ordered (group, weight tile,
-// row block).  Workgroups that run side by side on one XCD then share weight
-// tiles (across an expert's row blocks) and token rows (across weight tiles)
-// through that XCD's L2.
+// XCD-aware order: block b runs on XCD b % 8.  Work items, ordered (group,
+// weight tile, row block), are dealt to the XCDs in chunks of 32 in turn.
+// Workgroups that run side by side on one XCD then share weight tiles
+// (across an expert's row blocks, which the dispatch cuts to nearly equal
+// heights so that they keep pace) and token rows (across weight tiles)
+// through that XCD's L2, and no XCD is left with all of a heavy group.
 #include <type_traits>
 
 #include "smoe_internal.h"
@@ -73,14 +75,13 @@ struct LdsGemmParams {
 
 namespace {
 
-constexpr int kRows = 192;            // token rows per row block (the plan's bn)
+constexpr int kRows = 192;            // token rows per row block at most (the plan's bn)
 constexpr int kFR = 2;                // 32-row weight fragments per wave
 constexpr int kKC = 4;                // 16-wide k chunks per 64-wide stage
-constexpr int kTL = kRows / 8 / 4;    // token loads per wave per stage (8 rows each)
-constexpr int kLoads = kFR * kKC + kTL;  // vector-memory ops per wave per stage
 constexpr int kStage = kRows * 128;   // token bytes per stage
 constexpr int kWSlots = 3;            // weight register ring slots
-constexpr int kTSlots = 2;            // LDS ring slots (and token staging buffers)
+constexpr int kTSlots = 2;            // LDS ring slots
+constexpr int kChunk = 32;            // consecutive work items per XCD turn
 
 __device__ inline uint32_t pack_bf16x2_l(float a, float b) {
   const __bf16 ha = (__bf16)a, hb = (__bf16)b;
@@ -115,6 +116,10 @@ template <int MODE, int NA>
 __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowBlock& blk,
                                               bool shared, int col0, int nst,
                                               unsigned char (*ring)[kStage]) {
+  // token loads per wave per stage (8 rows each): the 4 waves bring the
+  // 32 NA rows of the fragments in use
+  constexpr int kTL = NA;
+  constexpr int kLoads = kFR * kKC + kTL;   // vector-memory ops per wave per stage
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int l31 = lane & 31, hi = lane >> 5;
@@ -142,7 +147,8 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     }
   }
   // tokens: load i of this wave brings rows 8 g .. 8 g + 7 (g = wave*kTL + i),
-  // 8 lanes per row; rows past the block repeat its last row
+  // 8 lanes per row; rows past the block (inside its last fragment) repeat
+  // its last row
   const uint16_t* tsrc[kTL];
 #pragma unroll
   for (int i = 0; i < kTL; ++i) {
@@ -334,14 +340,14 @@ template <int MODE>
 __global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kTSlots][kStage];
 
-  // XCD-aware deal of work items; items run in (group, weight tile, row
-  // block) order, so the row blocks that share a weight tile and the tiles
-  // that share a row block run side by side on one XCD and meet in its L2
+  // XCD-aware deal of work items, ordered (group, weight tile, row block):
+  // the items are cut in chunks of kChunk, dealt to the 8 XCDs in turn, so
+  // the row blocks that share a weight tile and the tiles that share a row
+  // block run side by side on one XCD and meet in its L2, while the work of
+  // heavy groups (the shared expert, hot experts) spreads over all XCDs
   const int n_items = *P.n_rb * P.tiles;
-  const int per = (n_items + 7) >> 3;
-  const int slot_b = blockIdx.x >> 3;
-  if (slot_b >= per) return;
-  const int item = (blockIdx.x & 7) * per + slot_b;
+  const int slot_b = blockIdx.x >> 3;   // this XCD's slot_b-th workgroup
+  const int item = ((slot_b / kChunk) * 8 + (blockIdx.x & 7)) * kChunk + slot_b % kChunk;
   if (item >= n_items) return;
   // a group's items fill [first * tiles, (first + n_group) * tiles)
   const RowBlock any = P.rb[item / P.tiles];
@@ -366,11 +372,12 @@ __global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
   }
 }
 
-// grid: enough blocks for every (row block, weight tile) item, rounded up to
-// a multiple of the 8 XCDs
+// grid: every chunk of kChunk (row block, weight tile) items up to the
+// row-block bound gets kChunk workgroups on its XCD; 8 XCDs per turn
 static unsigned lds_grid(const Plan& p, int tiles) {
   const long long items = (long long)p.rb_max * tiles;
-  return (unsigned)((items + 7) / 8 * 8);
+  const long long turns = ((items + kChunk - 1) / kChunk + 7) / 8;
+  return (unsigned)(turns * 8 * kChunk);
 }
 
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s) {

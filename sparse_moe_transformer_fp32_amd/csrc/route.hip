@@ -283,7 +283,8 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
 //            per expert marks which tokens of the chunk chose it, and a
 //            token's rank is the popcount of the mask bits below it.
 //   row blocks  work list for the grouped GEMMs: each expert's rows cut into
-//            blocks of at most `bn`, then the shared expert's T rows.
+//            ceil(count / bn) blocks of nearly equal height (whole granules
+//            of rows), then the shared expert's T rows cut the same way.
 __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -313,12 +314,26 @@ __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   return ex;
 }
 
+// Block i of the n_blk = ceil(cnt / bn) row blocks of a group with cnt rows.
+// The rows are cut in whole granules of g rows (g divides bn), and the
+// blocks' granule counts differ by at most one, so every block holds at most
+// bn rows, at least one, and the last one takes the ragged end.  Blocks of
+// one group then have (nearly) the same height: the workgroups that stream
+// the same weight tile for them run at the same pace and share it in L2.
+__device__ inline void split_block(int cnt, int n_blk, int g, int i, int* start, int* n) {
+  const int F = (cnt + g - 1) / g;
+  const int q = F / n_blk, r = F % n_blk;
+  const int st = g * (i * q + min(i, r));
+  *start = st;
+  *n = min(g * (q + (i < r ? 1 : 0)), cnt - st);
+}
+
 // counts, offsets (exclusive scan) and the GEMM row-block list from one
 // expert count per thread of a 1024-thread workgroup; returns this thread's
 // offset.  Every thread must call it.
-__device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int has_shared,
-                                    int rb_max, int* s_wave, int32_t* counts, int32_t* offsets,
-                                    RowBlock* rb, int32_t* n_rb) {
+__device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int gran,
+                                    int has_shared, int rb_max, int* s_wave, int32_t* counts,
+                                    int32_t* offsets, RowBlock* rb, int32_t* n_rb) {
   const int tid = threadIdx.x;
   const int KT = T * K;
   int total;
@@ -331,14 +346,18 @@ __device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int ha
     offsets[tid] = off;
     for (int i = 0; i < nrb; ++i) {
       const int p = rbpos + i;
-      if (p < rb_max) rb[p] = RowBlock{tid, off + i * bn, min(bn, cnt - i * bn), rbpos, nrb, {0, 0, 0}};
+      int st, n;
+      split_block(cnt, nrb, gran, i, &st, &n);
+      if (p < rb_max) rb[p] = RowBlock{tid, off + st, n, rbpos, nrb, {0, 0, 0}};
     }
   }
   if (tid == 0) offsets[E] = total;
   const int nrb_s = has_shared ? (T + bn - 1) / bn : 0;
   for (int i = tid; i < nrb_s; i += blockDim.x) {
     const int p = rb_total + i;
-    if (p < rb_max) rb[p] = RowBlock{E, KT + i * bn, min(bn, T - i * bn), rb_total, nrb_s, {0, 0, 0}};
+    int st, n;
+    split_block(T, nrb_s, gran, i, &st, &n);
+    if (p < rb_max) rb[p] = RowBlock{E, KT + st, n, rb_total, nrb_s, {0, 0, 0}};
   }
   if (tid == 0) n_rb[0] = min(rb_total + nrb_s, rb_max);
   return off;
@@ -347,7 +366,7 @@ __device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int ha
 struct DispatchArgs {
   const int32_t* topk_idx;
   const float* topk_w;
-  int T, K, E, bn, has_shared, rb_max;
+  int T, K, E, bn, gran, has_shared, rb_max;
   int32_t *counts, *offsets, *perm, *slot_pos, *row_token;
   float* row_w;
   RowBlock* rb;
@@ -377,8 +396,8 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs a) {
 
   // E <= 1024: one expert per thread
   const int cnt = tid < E ? s_cnt[tid] : 0;
-  const int off = finish_counts(cnt, E, T, K, a.bn, a.has_shared, a.rb_max, s_wave, a.counts,
-                                a.offsets, a.rb, a.n_rb);
+  const int off = finish_counts(cnt, E, T, K, a.bn, a.gran, a.has_shared, a.rb_max, s_wave,
+                                a.counts, a.offsets, a.rb, a.n_rb);
   if (tid < E) s_fill[tid] = off;
   __syncthreads();
 
@@ -478,8 +497,8 @@ __global__ __launch_bounds__(256) void dispatch_local_kernel(const int32_t* __re
 }
 
 __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
-    const int32_t* __restrict__ hist, int nblk, int T, int K, int E, int bn, int has_shared,
-    int rb_max, int32_t* __restrict__ block_base, int32_t* __restrict__ counts,
+    const int32_t* __restrict__ hist, int nblk, int T, int K, int E, int bn, int gran,
+    int has_shared, int rb_max, int32_t* __restrict__ block_base, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, RowBlock* __restrict__ rb, int32_t* __restrict__ n_rb) {
   __shared__ int s_wave[36];
   const int tid = threadIdx.x;
@@ -498,7 +517,7 @@ __global__ __launch_bounds__(1024) void dispatch_scan_kernel(
       }
     }
   }
-  finish_counts(cnt, E, T, K, bn, has_shared, rb_max, s_wave, counts, offsets, rb, n_rb);
+  finish_counts(cnt, E, T, K, bn, gran, has_shared, rb_max, s_wave, counts, offsets, rb, n_rb);
 }
 
 __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
@@ -566,7 +585,8 @@ hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
     hipLaunchKernelGGL(dispatch_local_kernel, dim3(nblk), dim3(256), (size_t)p.E * 8 * 4, s,
                        r.topk_idx, p.T, p.K, p.E, r.lrank, r.hist);
     hipLaunchKernelGGL(dispatch_scan_kernel, dim3(1), dim3(1024), 0, s, r.hist, nblk, p.T, p.K,
-                       p.E, p.bn, has_shared, p.rb_max, r.block_base, r.counts, r.offsets, r.rb,
+                       p.E, p.bn, p.rb_gran, has_shared, p.rb_max, r.block_base, r.counts,
+                       r.offsets, r.rb,
                        r.n_rb);
     hipLaunchKernelGGL(dispatch_scatter_kernel, dim3((p.KT + 255) / 256), dim3(256), 0, s,
                        r.topk_idx, r.topk_w, r.lrank, r.block_base, r.offsets, p.T, p.K, p.E,
@@ -576,7 +596,7 @@ hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
   DispatchArgs a{};
   a.topk_idx = r.topk_idx;
   a.topk_w = r.topk_w;
-  a.T = p.T; a.K = p.K; a.E = p.E; a.bn = p.bn; a.has_shared = has_shared;
+  a.T = p.T; a.K = p.K; a.E = p.E; a.bn = p.bn; a.gran = p.rb_gran; a.has_shared = has_shared;
   a.rb_max = p.rb_max;
   a.counts = r.counts; a.offsets = r.offsets; a.perm = r.perm; a.slot_pos = r.slot;
   a.row_token = r.row_token; a.row_w = r.row_w; a.rb = r.rb; a.n_rb = r.n_rb;
@@ -592,9 +612,10 @@ hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
 // s: every token t is row s*T + t of group s with weight 1, and slot s of
 // token t points at that row, so the combine adds the S partial outputs of
 // a token in slice order.  Blocks of one slice are consecutive.
-__global__ __launch_bounds__(256) void dense_rows_kernel(int T, int S, int bn, int32_t* row_token,
-                                                         float* row_w, int32_t* slot_pos,
-                                                         RowBlock* rb, int32_t* n_rb) {
+__global__ __launch_bounds__(256) void dense_rows_kernel(int T, int S, int bn, int gran,
+                                                         int32_t* row_token, float* row_w,
+                                                         int32_t* slot_pos, RowBlock* rb,
+                                                         int32_t* n_rb) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int per = (T + bn - 1) / bn;   // blocks per slice
   if (i < S * T) {
@@ -607,8 +628,10 @@ __global__ __launch_bounds__(256) void dense_rows_kernel(int T, int S, int bn, i
     const int sl = i / per, b = i - sl * per;
     RowBlock blk{};
     blk.group = sl;
-    blk.row_start = sl * T + b * bn;
-    blk.n_rows = min(bn, T - b * bn);
+    int st, n;
+    split_block(T, per, gran, b, &st, &n);
+    blk.row_start = sl * T + st;
+    blk.n_rows = n;
     blk.first = sl * per;
     blk.n_group = per;
     rb[i] = blk;
@@ -621,7 +644,7 @@ hipError_t launch_dense_rows(const Plan& p, int32_t* row_token, float* row_w, in
   // p.E = p.K = S slices, p.KT = S * T rows
   const int n = p.KT;
   hipLaunchKernelGGL(dense_rows_kernel, dim3((n + 255) / 256), dim3(256), 0, s, p.T, p.E, p.bn,
-                     row_token, row_w, slot_pos, rb, n_rb);
+                     p.rb_gran, row_token, row_w, slot_pos, rb, n_rb);
   return hipGetLastError();
 }
 

@@ -38,7 +38,8 @@ struct Plan {
   int32_t route_splits;  // split of H across router workgroups
   int32_t dispatch_blocks;  // > 0: three-kernel dispatch over this many 256-token blocks
   int32_t nb;            // 16-token column blocks per GEMM tile (1, 2, 4; 12 = LDS kernels)
-  int32_t bn;            // rows per row block = 16 * nb
+  int32_t bn;            // rows per row block at most = 16 * nb
+  int32_t rb_gran;       // row blocks are cut in whole granules of this many rows
   int32_t rb_max;        // upper bound on row blocks
   int32_t ksplit_gu;     // waves splitting K in the gate/up GEMM
   int32_t ksplit_dn;     // waves splitting K in the down GEMM
