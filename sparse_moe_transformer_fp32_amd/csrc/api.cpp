@@ -185,11 +185,20 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
   // router: 16-token tiles for decode, 64 otherwise; split H until the
   // launch has ~1024 workgroups (each split keeps >= 256 columns) so that
   // loads of many waves overlap
-  p->route_tok = T <= 16 ? 16 : 64;
-  const int tiles = ((T + p->route_tok - 1) / p->route_tok) * ((E + 63) / 64);
   int S = 1;
-  const int min_cols = T <= 64 ? 128 : 256;
-  while (S < 32 && tiles * S < 1024 && H % (2 * S * min_cols) == 0) S *= 2;
+  if (T >= 1024 && H % 64 == 0) {
+    // many tokens: 256-token x 48-expert tiles (from 1024 tokens on they beat
+    // the 64-token tiles on MI355X); split H while the launch stays within
+    // two workgroups per CU
+    p->route_tok = 256;
+    const int tiles = ((T + 255) / 256) * ((E + 47) / 48);
+    while (S < 8 && tiles * 2 * S <= 512 && H % (2 * S * 64) == 0) S *= 2;
+  } else {
+    p->route_tok = T <= 16 ? 16 : 64;
+    const int tiles = ((T + p->route_tok - 1) / p->route_tok) * ((E + 63) / 64);
+    const int min_cols = T <= 64 ? 128 : 256;
+    while (S < 32 && tiles * S < 1024 && H % (2 * S * min_cols) == 0) S *= 2;
+  }
   p->route_splits = S;
 
   // dispatch: one workgroup for small T, three kernels over 256-token blocks

@@ -10,6 +10,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace smoe {
 
 // --------------------------------------------------------------------------
@@ -121,6 +123,168 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
       const int e = e0 + 4 * g + j;
       if (e < E) partial[((size_t)t * E + e) * S + split] = acc[nb][j];
     }
+  }
+}
+
+// --------------------------------------------------------------------------
+// Router logits for many tokens, with the same fp32 semantics.
+//
+// Workgroup tile: 48 experts x 256 tokens over one split of H.  Wave w owns
+// tokens 64w..64w+63 as four 16-token B fragments, loaded from x straight
+// into registers (no other wave reads them), and all 48 experts as three
+// 16-row A fragments per bf16 part, read from LDS.  Per 64-wide k stage the
+// workgroup loads the fp32 weights of its experts once, splits each into its
+// three bf16 parts (as above) and stores them to LDS in A-fragment order, so
+// a weight is split once per 256 tokens.  Per 32-wide k step the parts are
+// applied lo, mid, hi, as in the kernel above.
+constexpr int kRouteE = 48;    // experts per workgroup (three 16-row fragments)
+constexpr int kRouteT = 256;   // tokens per workgroup (64 per wave)
+
+__global__ __launch_bounds__(256, 2) void route_logits_wide_kernel(
+    const uint16_t* __restrict__ x, const float* __restrict__ W, float* __restrict__ partial,
+    int T, int H, int E, int klen) {
+  // A fragments of one stage: [slot][32-k chunk][part lo/mid/hi][fragment][lane] x 16 bytes
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[2][2][3][3][1024];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int e0 = blockIdx.y * kRouteE;
+  const int t0 = blockIdx.x * kRouteT + wave * 64;
+  const int split = blockIdx.z;
+  const int kb = split * klen;
+  const int nst = klen / 64;
+
+  // weights: load m of a thread brings row 16 m + tid / 16 of the tile, k =
+  // 4 (tid % 16) .. +3 of the stage (16 threads read a row's 256 bytes).
+  // In A-fragment order those 4 values are half (q % 2) of lane
+  // 16 ((q % 8) / 2) + tid / 16 of chunk q / 8, q = tid % 16.
+  const float* wsrc[3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+    wsrc[m] = W + (size_t)min(e0 + 16 * m + (tid >> 4), E - 1) * H + kb + 4 * (tid & 15);
+  const int q = tid & 15;
+  const int a_off = (q >> 3) * (3 * 3 * 1024) + (16 * ((q & 7) >> 1) + (tid >> 4)) * 16 + 8 * (q & 1);
+  // tokens: B fragment n of chunk c is token t0 + 16 n + lane % 16, k = 32 c
+  // + 8 (lane / 16) .. +7 of the stage
+  const uint16_t* xsrc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n)
+    xsrc[n] = x + (size_t)min(t0 + 16 * n + (lane & 15), T - 1) * H + kb + 8 * (lane >> 4);
+
+  f32x4 acc[3][4];
+#pragma unroll
+  for (int m = 0; m < 3; ++m)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // past the end of K every load re-reads the last stage (in bounds; unused)
+  auto load_w = [&](f32x4 (&w)[3], int st) {
+    const int off = min(st, nst - 1) * 64;
+#pragma unroll
+    for (int m = 0; m < 3; ++m) w[m] = *reinterpret_cast<const f32x4*>(wsrc[m] + off);
+  };
+  auto load_x = [&](u32x4 (&v)[2][4], int st) {
+    const int off = min(st, nst - 1) * 64;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int n = 0; n < 4; ++n) v[c][n] = *reinterpret_cast<const u32x4*>(xsrc[n] + off + 32 * c);
+  };
+  // split the loaded weights and store the parts to LDS slot `slot`
+  auto store_w = [&](const f32x4 (&w)[3], int slot) {
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      uint32_t hi2[2], mid2[2], lo2[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        uint16_t hb[2], mb[2], lb[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const float wv = w[m][2 * i + j];
+          const __bf16 h = (__bf16)wv;
+          const float r1 = wv - (float)h;
+          const __bf16 md = (__bf16)r1;
+          const float r2 = r1 - (float)md;
+          hb[j] = __builtin_bit_cast(uint16_t, h);
+          mb[j] = __builtin_bit_cast(uint16_t, md);
+          lb[j] = __builtin_bit_cast(uint16_t, (__bf16)r2);
+        }
+        hi2[i] = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+        mid2[i] = (uint32_t)mb[0] | ((uint32_t)mb[1] << 16);
+        lo2[i] = (uint32_t)lb[0] | ((uint32_t)lb[1] << 16);
+      }
+      unsigned char* base = &s_a[slot][0][0][m][0] + a_off;
+      *reinterpret_cast<u32x2*>(base + 0 * 3 * 1024) = u32x2{lo2[0], lo2[1]};
+      *reinterpret_cast<u32x2*>(base + 1 * 3 * 1024) = u32x2{mid2[0], mid2[1]};
+      *reinterpret_cast<u32x2*>(base + 2 * 3 * 1024) = u32x2{hi2[0], hi2[1]};
+    }
+  };
+  auto compute = [&](int slot, const u32x4 (&v)[2][4]) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 a[3][3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+          a[p][m] = *reinterpret_cast<const u32x4*>(&s_a[slot][c][p][m][lane * 16]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int m = 0; m < 3; ++m)
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[p][m]), __builtin_bit_cast(bf16x8, v[c][n]),
+                acc[m][n], 0, 0, 0);
+    }
+  };
+
+  // stage s: weights of s+1 into registers (split into LDS slot (s+1)%2 at
+  // the end of the stage), tokens of s+2 into buffer (s+2)%3; LDS slot
+  // (s+1)%2 was last read in stage s-1, before its closing barrier
+  f32x4 wreg[3];
+  u32x4 xb[3][2][4];
+  load_w(wreg, 0);
+  load_x(xb[0], 0);
+  load_x(xb[1], 1);
+  store_w(wreg, 0);
+  __syncthreads();
+  auto stage = [&](auto jc, int st) {
+    constexpr int J = decltype(jc)::value;   // st % 6
+    load_w(wreg, st + 1);
+    load_x(xb[(J + 2) % 3], st + 2);
+    compute(J % 2, xb[J % 3]);
+    store_w(wreg, (J + 1) % 2);
+    __syncthreads();
+  };
+  int st = 0;
+  for (; st + 6 <= nst; st += 6) {
+    stage(std::integral_constant<int, 0>{}, st);
+    stage(std::integral_constant<int, 1>{}, st + 1);
+    stage(std::integral_constant<int, 2>{}, st + 2);
+    stage(std::integral_constant<int, 3>{}, st + 3);
+    stage(std::integral_constant<int, 4>{}, st + 4);
+    stage(std::integral_constant<int, 5>{}, st + 5);
+  }
+  if (st < nst) stage(std::integral_constant<int, 0>{}, st);
+  if (st + 1 < nst) stage(std::integral_constant<int, 1>{}, st + 1);
+  if (st + 2 < nst) stage(std::integral_constant<int, 2>{}, st + 2);
+  if (st + 3 < nst) stage(std::integral_constant<int, 3>{}, st + 3);
+  if (st + 4 < nst) stage(std::integral_constant<int, 4>{}, st + 4);
+
+  // accumulator register j of fragment (m, n): expert 16 m + 4 (lane / 16) + j,
+  // token 16 n + lane % 16; partial sums stored [T][E][S]
+  const int S = gridDim.z;
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int t = t0 + 16 * n + (lane & 15);
+    if (t >= T) continue;
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 16 * m + 4 * (lane >> 4) + j;
+        if (e < E) partial[((size_t)t * E + e) * S + split] = acc[m][n][j];
+      }
   }
 }
 
@@ -547,6 +711,13 @@ __global__ __launch_bounds__(256) void dispatch_scatter_kernel(
 hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
                                float* partial, hipStream_t s) {
   const int klen = p.H / p.route_splits;
+  if (p.route_tok == kRouteT) {
+    if (klen % 64) return hipErrorInvalidValue;
+    dim3 grid((p.T + kRouteT - 1) / kRouteT, (p.E + kRouteE - 1) / kRouteE, p.route_splits);
+    hipLaunchKernelGGL(route_logits_wide_kernel, grid, dim3(256), 0, s, x, W, partial, p.T, p.H,
+                       p.E, klen);
+    return hipGetLastError();
+  }
   dim3 grid((p.T + p.route_tok - 1) / p.route_tok, (p.E + 63) / 64, p.route_splits);
   if (p.route_tok == 16)
     hipLaunchKernelGGL((route_logits_kernel<1, 4>), grid, dim3(256), 0, s, x, W, partial, p.T,

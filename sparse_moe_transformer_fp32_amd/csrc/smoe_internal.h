@@ -34,7 +34,7 @@ struct Plan {
   int32_t T, H, E, K, I, Is;
   int32_t KT;            // T*K routed rows
   int32_t rows_total;    // KT + (Is > 0 ? T : 0)
-  int32_t route_tok;     // tokens per router tile (16 or 64)
+  int32_t route_tok;     // tokens per router tile (16 or 64; 256: the wide kernel)
   int32_t route_splits;  // split of H across router workgroups
   int32_t dispatch_blocks;  // > 0: three-kernel dispatch over this many 256-token blocks
   int32_t nb;            // 16-token column blocks per GEMM tile (1, 2, 4; 12 = LDS kernels)

@@ -2,7 +2,8 @@
 
 Small cases cover every tiling variant (row blocks of 16/32/64 tokens with
 split-K 1/2/4 in the register-streaming kernels, 192-token blocks in the
-LDS-pipelined kernels, and the fallback when shapes exclude them), ragged tails, T=1, K=1, K=E, E not a multiple of 64, the
+LDS-pipelined kernels, and the fallback when shapes exclude them; the
+64-token and the 256-token router tiles), ragged tails, T=1, K=1, K=E, E not a multiple of 64, the
 largest E and K, no shared expert, the SwiGLU clamp and the alternative bias
 reading.  Flash-shaped cases run the same launch configuration as the
 benchmark: full outputs at T=16 and sampled rows at T=4096/8192.
@@ -88,6 +89,7 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "lds_multi_block": (113, 1000, 256, 6, 2, 128, 128),
     "dispatch_blocks_ragged": (115, 1500, 256, 16, 4, 128, 64),
     "dispatch_blocks_E1024": (116, 1300, 256, 1024, 16, 64, 64),
+    "wide_router_E100": (117, 1100, 2048, 100, 6, 128, 128),
 }
 
 
