@@ -123,8 +123,11 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_stats(csv_path, out_path, command, regex="smoe"):
-    """Short text summary of a rocprofv3 --stats kernel table."""
+def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
+    """Short text summary of a rocprofv3 --stats kernel table; with the
+    run's kernel trace, also per launch shape (kernel, grid), since one
+    kernel serves several workloads of one run (e.g. the T=16 MoE layer and
+    the dense FFN side measurement launch the same register-streaming GEMM)."""
     rows = [r for r in _read_csv(csv_path) if re.search(regex, r["Name"])]
     lines = [f"# rocprofv3 kernel statistics ({os.path.basename(csv_path)})",
              f"# command: {command}",
@@ -133,6 +136,26 @@ def summarize_stats(csv_path, out_path, command, regex="smoe"):
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"{int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
                      f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f}  {r['Name']}")
+    if trace_csv:
+        import collections
+        groups = collections.defaultdict(list)
+        for r in _read_csv(trace_csv):
+            name = r.get("Kernel_Name", "")
+            if not re.search(regex, name):
+                continue
+            try:   # grid sizes are in work-items per dimension
+                n_wg = 1
+                for ax in "XYZ":
+                    n_wg *= int(r.get(f"Grid_Size_{ax}") or 1) // max(1, int(r.get(f"Workgroup_Size_{ax}") or 1))
+            except ValueError:
+                n_wg = "?"
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups[(name, n_wg)].append(dur)
+        lines += ["", f"# per launch shape, from the kernel trace ({os.path.basename(trace_csv)})",
+                  f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'wgs':>7}  kernel"]
+        for (name, n_wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"{len(d):6d} {sum(d) / len(d):10.2f} {min(d):10.2f} {max(d):10.2f} "
+                         f"{n_wg!s:>7}  {name}")
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -384,8 +407,9 @@ def main():
                          "known-size reference for HBM byte counters) and exit")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-FFN side measurements of the default run")
-    ap.add_argument("--summarize-stats", nargs=3, metavar=("CSV", "OUT", "COMMAND"),
-                    help="offline: write a short summary of a rocprofv3 kernel_stats.csv")
+    ap.add_argument("--summarize-stats", nargs="+", metavar="ARG",
+                    help="offline: STATS_CSV OUT COMMAND [TRACE_CSV] -> a short summary of "
+                         "a rocprofv3 kernel_stats.csv (and of its kernel trace per launch shape)")
     ap.add_argument("--write-traffic", nargs="+", metavar="ARG",
                     help="offline: PMC_ROOT COMMAND... -> profiles/traffic.json")
     args = ap.parse_args()
