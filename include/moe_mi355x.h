@@ -67,7 +67,10 @@ typedef enum {
 } moe_status;
 
 /* Layer sizes (host struct).
- *   T  tokens, 1 <= T <= 1<<20
+ *   T  tokens, 0 <= T <= 1<<20.  T = 0 is an empty batch: a call reads and
+ *      writes no array with a T dimension (those pointers may be NULL; the
+ *      rest are checked as usual), moe_route and a routing output still
+ *      receive counts = 0 and offsets = 0, and moe_expert_stats rejects it
  *   H  hidden size, a multiple of 128, 128 <= H <= 16384     (Flash: 4096)
  *   E  routed experts, 1 <= E <= 1024                          (Flash: 288)
  *   K  experts per token, 1 <= K <= min(E, 16)                 (Flash: 8)
@@ -186,8 +189,8 @@ int32_t moe_abi_version(void);
  * library; valid until the next call on this thread; "" after success). */
 const char* moe_last_error(void);
 
-/* Workspace bytes that moe_route and moe_forward need for `d` (host).
- * Returns 0 if `d` is NULL or out of range. */
+/* Workspace bytes that moe_route and moe_forward need for `d` (host; > 0,
+ * also for T = 0).  Returns 0 if `d` is NULL or out of range. */
 size_t moe_workspace_bytes(const moe_dims* d);
 
 /* Offsets of h and o in a workspace for `d`.  Returns MOE_ERR_NULL or
@@ -243,7 +246,8 @@ moe_status moe_pack_weights_strided(const uint16_t* src, uint16_t* dst, int32_t 
 
 /* Glue between chained layers of a pre-norm residual stream (paperlayer.ai
  * summary, App. B: RMSNorm over the summed layer outputs; model card:
- * zero_centered).  For each of the T rows of width H:
+ * zero_centered).  For each of the T rows of width H (T = 0: nothing to do,
+ * the pointers are not checked):
  *   r      = r_in + y_add            (fp32 add, stored to r_out as bf16;
  *                                     y_add may be NULL: r = r_in)
  *   x_out  = bf16( r' / sqrt(mean(r'^2) + eps) * (1 + gamma) )
@@ -262,7 +266,7 @@ moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
  * to r_in in fp32 before the one rounding, so it is never stored on its own.
  * x is the layer's (already normalised) input; it must not alias r_in or
  * r_out.  Other arguments, the workspace and the errors are as for
- * moe_forward; res and its r_in, r_out must be non-NULL. */
+ * moe_forward; res and, unless T = 0, its r_in, r_out must be non-NULL. */
 moe_status moe_forward_residual(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
                                 const moe_router* router, const moe_experts* experts,
                                 const moe_shared* shared, const moe_residual* res,
@@ -292,7 +296,7 @@ moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint1
                          const moe_ffn* ffn, float swiglu_limit, uint16_t* y, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
-/* Per-expert activation statistics for monitoring (paperlayer.ai summary,
+/* Per-expert activation statistics for monitoring (T >= 1; paperlayer.ai summary,
  * §4.1.2 and §4.1.3: per-expert activation norms, whose maximum-to-median
  * ratio exposes localized blow-up and whose falling minimum-to-median ratio
  * warns of expert death; App. B: the blow-up is in the SwiGLU product h).

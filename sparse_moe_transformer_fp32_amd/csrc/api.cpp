@@ -47,8 +47,8 @@ size_t align_up(size_t v) { return (v + 255) & ~(size_t)255; }
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 moe_status check_shape(const moe_dims* d) {
-  if (d->T < 1 || d->T > (1 << 20))
-    return fail(MOE_ERR_SHAPE, "T=%d out of range [1, 1048576]", d->T);
+  if (d->T < 0 || d->T > (1 << 20))
+    return fail(MOE_ERR_SHAPE, "T=%d out of range [0, 1048576]", d->T);
   if (d->H < 128 || d->H > 16384 || d->H % 128)
     return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", d->H);
   if (d->E < 1 || d->E > 1024) return fail(MOE_ERR_SHAPE, "E=%d out of range [1, 1024]", d->E);
@@ -62,7 +62,7 @@ moe_status check_shape(const moe_dims* d) {
 }
 
 moe_status check_dense(int T, int H, int I, int S) {
-  if (T < 1 || T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T=%d out of range [1, 1048576]", T);
+  if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T=%d out of range [0, 1048576]", T);
   if (H < 128 || H > 16384 || H % 128)
     return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", H);
   if (S < 1 || S > 16) return fail(MOE_ERR_SHAPE, "S=%d out of range [1, 16]", S);
@@ -157,11 +157,18 @@ RouteBufs bufs_from_ws(const smoe::Plan& p, char* ws) {
                    nullptr};
 }
 
-moe_status check_routing_out(const moe_routing* r, bool for_route) {
-  if (!r->topk_idx || !r->topk_w || !r->counts || !r->offsets || !r->perm_token || !r->slot_pos)
+// An empty batch (T = 0) writes only counts and offsets.
+moe_status check_routing_out(const moe_routing* r, bool for_route, bool empty) {
+  if (!r->counts || !r->offsets ||
+      (!empty && (!r->topk_idx || !r->topk_w || !r->perm_token || !r->slot_pos)))
     return fail(MOE_ERR_NULL, "%s: routing output members must be non-NULL (keys/scores optional)",
                 for_route ? "moe_route" : "moe_forward");
   return MOE_OK;
+}
+
+// counts = 0 and offsets = 0: the routing of an empty batch
+moe_status route_empty(int E, const moe_routing* r, hipStream_t s) {
+  return launched(smoe::launch_zero_counts(r->counts, r->offsets, E, s), "zero_counts");
 }
 
 moe_status check_routing_align(const moe_routing* r) {
@@ -293,9 +300,9 @@ moe_status moe_workspace_layout(const moe_dims* d, moe_ws_layout* out) {
 moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
                      const moe_router* router, const moe_routing* out, void* ws, size_t ws_bytes,
                      hipStream_t stream) {
-  if (!d || !x || !router || !router->W || !router->b || !out || !ws)
+  if (!d || !router || !router->W || !router->b || !out || !ws || (!x && d->T != 0))
     return fail(MOE_ERR_NULL, "moe_route: NULL argument (dims, x, router, router->W/b, out, ws)");
-  moe_status st = check_routing_out(out, true);
+  moe_status st = check_routing_out(out, true, d->T == 0);
   if (st) return st;
   if ((st = check_shape(d))) return st;
   if ((st = check_opts(opts))) return st;
@@ -307,6 +314,10 @@ moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
   if (ws_bytes < p.ws_total)
     return fail(MOE_ERR_WORKSPACE, "moe_route: workspace %zu bytes < required %zu", ws_bytes,
                 p.ws_total);
+  if (d->T == 0) {
+    if ((st = route_empty(d->E, out, stream))) return st;
+    return ok();
+  }
   const moe_opts o = opts ? *opts : default_opts();
   if ((st = run_route(p, o, x, router, bufs_from(out), static_cast<char*>(ws), stream))) return st;
   return ok();
@@ -325,7 +336,7 @@ moe_status check_forward(const char* fn, const moe_dims* d, const moe_opts* opts
   moe_status st;
   if (d->Is > 0 && (!shared || !shared->w_gate || !shared->w_up || !shared->w_down))
     return fail(MOE_ERR_NULL, "%s: Is=%d but the shared expert weights are NULL", fn, d->Is);
-  if (routing_out && (st = check_routing_out(routing_out, false))) return st;
+  if (routing_out && (st = check_routing_out(routing_out, false, d->T == 0))) return st;
   if ((st = check_shape(d))) return st;
   if ((st = check_opts(opts))) return st;
   if (misaligned(x) || misaligned(router->W) || misaligned(router->b) ||
@@ -397,6 +408,11 @@ moe_status forward_impl(const char* fn, const moe_dims* d, const moe_opts* opts,
   if (ws_bytes < p.ws_total)
     return fail(MOE_ERR_WORKSPACE, "%s: workspace %zu bytes < required %zu", fn, ws_bytes,
                 p.ws_total);
+  if (d->T == 0) {   // empty batch: nothing to compute, routing output is empty
+    moe_status st;
+    if (routing_out && (st = route_empty(d->E, routing_out, stream))) return st;
+    return ok();
+  }
   const moe_opts o = opts ? *opts : default_opts();
   char* w = static_cast<char*>(ws);
   const RouteBufs rb = routing_out ? bufs_from(routing_out) : bufs_from_ws(p, w);
@@ -423,8 +439,8 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
                        const moe_router* router, const moe_experts* experts,
                        const moe_shared* shared, uint16_t* y, const moe_routing* routing_out,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (!d || !x || !router || !router->W || !router->b || !experts || !experts->w_gate ||
-      !experts->w_up || !experts->w_down || !y || !ws)
+  if (!d || !router || !router->W || !router->b || !experts || !experts->w_gate ||
+      !experts->w_up || !experts->w_down || !ws || ((!x || !y) && d->T != 0))
     return fail(MOE_ERR_NULL,
                 "moe_forward: NULL argument (dims, x, router, router->W/b, experts->w_*, y, ws)");
   moe_status st;
@@ -432,7 +448,7 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
     return st;
   if (misaligned(y) || misaligned(ws))
     return fail(MOE_ERR_ALIGN, "moe_forward: device pointers must be 16-byte aligned");
-  if (x == y) return fail(MOE_ERR_OPTION, "moe_forward: x and y must not alias");
+  if (x == y && d->T != 0) return fail(MOE_ERR_OPTION, "moe_forward: x and y must not alias");
   return forward_impl("moe_forward", d, opts, x, router, experts, shared, y, nullptr, routing_out,
                       ws, ws_bytes, stream);
 }
@@ -442,8 +458,9 @@ moe_status moe_forward_residual(const moe_dims* d, const moe_opts* opts, const u
                                 const moe_shared* shared, const moe_residual* res,
                                 const moe_routing* routing_out, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  if (!d || !x || !router || !router->W || !router->b || !experts || !experts->w_gate ||
-      !experts->w_up || !experts->w_down || !res || !res->r_in || !res->r_out || !ws)
+  if (!d || !router || !router->W || !router->b || !experts || !experts->w_gate ||
+      !experts->w_up || !experts->w_down || !res || !ws ||
+      ((!x || !res->r_in || !res->r_out) && d->T != 0))
     return fail(MOE_ERR_NULL,
                 "moe_forward_residual: NULL argument (dims, x, router, router->W/b, "
                 "experts->w_*, res, res->r_in/r_out, ws)");
@@ -456,9 +473,9 @@ moe_status moe_forward_residual(const moe_dims* d, const moe_opts* opts, const u
   if (misaligned(res->r_in) || misaligned(res->r_out) || misaligned(res->x_next) ||
       misaligned(res->gamma) || misaligned(ws))
     return fail(MOE_ERR_ALIGN, "moe_forward_residual: device pointers must be 16-byte aligned");
-  if (res->x_next && (res->x_next == res->r_out || res->x_next == res->r_in))
+  if (d->T != 0 && res->x_next && (res->x_next == res->r_out || res->x_next == res->r_in))
     return fail(MOE_ERR_OPTION, "moe_forward_residual: x_next must not alias r_in or r_out");
-  if (res->r_out == x || (const uint16_t*)res->r_in == x)
+  if (d->T != 0 && (res->r_out == x || (const uint16_t*)res->r_in == x))
     return fail(MOE_ERR_OPTION, "moe_forward_residual: x must not alias r_in or r_out");
   return forward_impl("moe_forward_residual", d, opts, x, router, experts, shared, nullptr, res,
                       routing_out, ws, ws_bytes, stream);
@@ -474,7 +491,7 @@ size_t moe_dense_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t S) {
 moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint16_t* x,
                          const moe_ffn* ffn, float swiglu_limit, uint16_t* y, void* ws,
                          size_t ws_bytes, hipStream_t stream) {
-  if (!x || !ffn || !ffn->w_gate || !ffn->w_up || !ffn->w_down || !y || !ws)
+  if (!ffn || !ffn->w_gate || !ffn->w_up || !ffn->w_down || !ws || ((!x || !y) && T != 0))
     return fail(MOE_ERR_NULL, "moe_dense_ffn: NULL argument (x, ffn, ffn->w_*, y, ws)");
   moe_status st;
   if ((st = check_dense(T, H, I, S))) return st;
@@ -483,12 +500,13 @@ moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint1
   if (misaligned(x) || misaligned(ffn->w_gate) || misaligned(ffn->w_up) ||
       misaligned(ffn->w_down) || misaligned(y) || misaligned(ws))
     return fail(MOE_ERR_ALIGN, "moe_dense_ffn: device pointers must be 16-byte aligned");
-  if (x == y) return fail(MOE_ERR_OPTION, "moe_dense_ffn: x and y must not alias");
+  if (x == y && T != 0) return fail(MOE_ERR_OPTION, "moe_dense_ffn: x and y must not alias");
   smoe::Plan p;
   smoe::make_plan(T, H, S, S, I / S, 0, &p);
   if (ws_bytes < p.ws_total)
     return fail(MOE_ERR_WORKSPACE, "moe_dense_ffn: workspace %zu bytes < required %zu", ws_bytes,
                 p.ws_total);
+  if (T == 0) return ok();   // empty batch
   char* w = static_cast<char*>(ws);
   int32_t* slot = reinterpret_cast<int32_t*>(w + p.ws_slot);
   {
@@ -517,6 +535,7 @@ moe_status moe_expert_stats(const moe_dims* d, const int32_t* offsets, const uin
     return fail(MOE_ERR_NULL, "moe_expert_stats: NULL argument (dims, offsets, h, stats)");
   moe_status st;
   if ((st = check_shape(d))) return st;
+  if (d->T < 1) return fail(MOE_ERR_SHAPE, "moe_expert_stats: T=0, an empty batch has no rows");
   if (misaligned(offsets) || misaligned(h) || misaligned(stats) || misaligned(ratios))
     return fail(MOE_ERR_ALIGN, "moe_expert_stats: device pointers must be 16-byte aligned");
   if ((st = launched(smoe::launch_expert_stats(d->T, d->E, d->K, d->I, d->Is, offsets, h, stats,
@@ -574,14 +593,15 @@ moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events) {
 moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
                                 const uint16_t* y_add, const float* gamma, float eps,
                                 uint16_t* r_out, uint16_t* x_out, hipStream_t stream) {
+  if (T < 0 || T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T=%d out of range [0, 1048576]", T);
+  if (H < 128 || H > 16384 || H % 128)
+    return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", H);
+  if (!isfinite(eps) || eps < 0.f) return fail(MOE_ERR_OPTION, "eps must be finite and >= 0");
+  if (T == 0) return ok();   // empty batch: no rows, the pointers are not used
   if (!r_in) return fail(MOE_ERR_NULL, "moe_residual_rmsnorm: r_in is NULL");
   if (y_add && !r_out && !x_out)
     return fail(MOE_ERR_NULL, "moe_residual_rmsnorm: y_add given but both r_out and x_out NULL");
   if (!y_add && !x_out) return fail(MOE_ERR_NULL, "moe_residual_rmsnorm: nothing to compute");
-  if (T < 1 || T > (1 << 20)) return fail(MOE_ERR_SHAPE, "T=%d out of range [1, 1048576]", T);
-  if (H < 128 || H > 16384 || H % 128)
-    return fail(MOE_ERR_SHAPE, "H=%d must be a multiple of 128 in [128, 16384]", H);
-  if (!isfinite(eps) || eps < 0.f) return fail(MOE_ERR_OPTION, "eps must be finite and >= 0");
   if (misaligned(r_in) || misaligned(y_add) || misaligned(gamma) || misaligned(r_out) ||
       misaligned(x_out))
     return fail(MOE_ERR_ALIGN, "moe_residual_rmsnorm: pointers must be 16-byte aligned");

@@ -776,6 +776,20 @@ hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
 }
 
 // --------------------------------------------------------------------------
+// The routing of an empty batch: every count and offset is 0.
+__global__ __launch_bounds__(256) void zero_counts_kernel(int32_t* counts, int32_t* offsets,
+                                                          int E) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < E) counts[i] = 0;
+  if (i <= E) offsets[i] = 0;
+}
+
+hipError_t launch_zero_counts(int32_t* counts, int32_t* offsets, int E, hipStream_t s) {
+  hipLaunchKernelGGL(zero_counts_kernel, dim3(E / 256 + 1), dim3(256), 0, s, counts, offsets, E);
+  return hipGetLastError();
+}
+
+// --------------------------------------------------------------------------
 // Row list of a dense gated FFN run through the grouped GEMMs (the dense
 // layers of the model; hyper.ai summary, 方法, and paperlayer.ai summary,
 // §2.2: the first layers use a dense FFN; model card: intermediate_size).

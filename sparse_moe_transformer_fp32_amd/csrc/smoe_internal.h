@@ -105,6 +105,9 @@ hipError_t launch_down(const Plan& p, const DownArgs& a, hipStream_t s);
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s);
 
+// counts[0..E) = 0 and offsets[0..E] = 0 (the routing of an empty batch)
+hipError_t launch_zero_counts(int32_t* counts, int32_t* offsets, int E, hipStream_t s);
+
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,
                        long long ld, long long mat_stride, hipStream_t s);
 

@@ -46,7 +46,8 @@ def test_workspace_sizes():
 
 
 @pytest.mark.parametrize("dims,frag", [
-    ((0, 4096, 288, 8, 1280, 1280), "T=0"),
+    ((-1, 4096, 288, 8, 1280, 1280), "T=-1"),
+    (((1 << 20) + 1, 4096, 288, 8, 1280, 1280), "T=1048577"),
     ((16, 4000, 288, 8, 1280, 1280), "H=4000"),
     ((16, 4096, 0, 8, 1280, 1280), "E=0"),
     ((16, 4096, 2000, 8, 1280, 1280), "E=2000"),
@@ -103,8 +104,8 @@ def test_forward_null_checks():
 def test_forward_check_order():
     # null is reported before shape, shape before options, options before alignment
     bad_opts = B.make_opts(route_scale=-1.0)
-    assert _forward(dims=(0,) + FLASH[1:], x=0, ws_bytes=1) == B.MOE_ERR_NULL
-    assert _forward(dims=(0,) + FLASH[1:], opts=bad_opts, ws_bytes=1) == B.MOE_ERR_SHAPE
+    assert _forward(dims=(16, 4000) + FLASH[2:], x=0, ws_bytes=1) == B.MOE_ERR_NULL
+    assert _forward(dims=(16, 4000) + FLASH[2:], opts=bad_opts, ws_bytes=1) == B.MOE_ERR_SHAPE
     assert _forward(opts=bad_opts, x=A + 2) == B.MOE_ERR_OPTION
     assert _forward(x=A + 2, ws_bytes=1) == B.MOE_ERR_ALIGN
 
@@ -153,7 +154,10 @@ def test_residual_rmsnorm_checks():
     f = lib.moe_residual_rmsnorm
     assert f(16, 4096, None, None, None, 1e-6, None, _vp(A), None) == B.MOE_ERR_NULL
     assert f(16, 4096, _vp(A), None, None, 1e-6, None, None, None) == B.MOE_ERR_NULL
-    assert f(0, 4096, _vp(A), None, None, 1e-6, None, _vp(A), None) == B.MOE_ERR_SHAPE
+    assert f(-1, 4096, _vp(A), None, None, 1e-6, None, _vp(A), None) == B.MOE_ERR_SHAPE
+    # an empty batch is a no-op (returns before any HIP call), pointers unused
+    assert f(0, 4096, None, None, None, 1e-6, None, None, None) == B.MOE_OK
+    assert f(0, 100, None, None, None, 1e-6, None, None, None) == B.MOE_ERR_SHAPE
     assert f(16, 100, _vp(A), None, None, 1e-6, None, _vp(A), None) == B.MOE_ERR_SHAPE
     assert f(16, 4096, _vp(A), None, None, -1.0, None, _vp(A), None) == B.MOE_ERR_OPTION
     assert f(16, 4096, _vp(A + 2), None, None, 1e-6, None, _vp(A), None) == B.MOE_ERR_ALIGN
@@ -225,7 +229,7 @@ def test_dense_checks():
     assert lib.moe_dense_workspace_bytes(16, 4096, 11264, 7) == 0       # 11264 % 7
     assert lib.moe_dense_workspace_bytes(16, 4096, 11264, 32) == 0      # S > 16
     assert lib.moe_dense_workspace_bytes(16, 4096, 11264 + 32, 8) == 0  # slices not % 64
-    assert lib.moe_dense_workspace_bytes(0, 4096, 11264, 8) == 0
+    assert lib.moe_dense_workspace_bytes(-1, 4096, 11264, 8) == 0
     need = lib.moe_dense_workspace_bytes(16, 4096, 11264, 8)
     f = B.Shared(_vp(A), _vp(A), _vp(A))
 
@@ -263,3 +267,28 @@ def test_pack_weights_strided_checks():
     assert f(_vp(A), _vp(1 << 30), 2, 16, 32, 64, -8, None) == B.MOE_ERR_SHAPE
     # the source spans (n-1)*stride + (rows-1)*ld + cols elements: overlap found
     assert f(_vp(A), _vp(A + 2 * (15 * 64 + 64) - 16), 2, 16, 32, 64, 32, None) == B.MOE_ERR_OPTION
+
+
+def test_empty_batch_host_paths():
+    """T = 0: workspace sizes stay positive, NULL T-sized pointers are
+    accepted, and calls that need no device work return MOE_OK before any
+    HIP call (the fake addresses are never touched)."""
+    assert B.workspace_bytes(0, *FLASH[1:]) > 0
+    lib = B.load()
+    assert lib.moe_dense_workspace_bytes(0, 4096, 11264, 8) > 0
+    empty = (0,) + FLASH[1:]
+    assert _forward(dims=empty, x=0, y=0) == B.MOE_OK
+    assert B.last_error() == ""
+    assert _forward(dims=empty, x=0, y=0, W=0) == B.MOE_ERR_NULL      # router still required
+    assert _forward(dims=empty, x=0, y=0, ws_bytes=10) == B.MOE_ERR_WORKSPACE
+    # a routing output for T = 0 needs only counts and offsets (which the
+    # call would zero on the device, so it is exercised on the GPU)
+    bad = B.Routing(None, None, None, _vp(A), None, None, None, None)
+    assert _forward(dims=empty, x=0, y=0, routing=bad) == B.MOE_ERR_NULL
+    ffn = B.Shared(_vp(A), _vp(A), _vp(A))
+    need = lib.moe_dense_workspace_bytes(0, 4096, 11264, 8)
+    assert lib.moe_dense_ffn(0, 4096, 11264, 8, None, ctypes.byref(ffn), 0.0, None, _vp(A), need,
+                             None) == B.MOE_OK
+    d = B.dims(*empty)
+    assert lib.moe_expert_stats(ctypes.byref(d), _vp(A), _vp(A), _vp(A), None,
+                                None) == B.MOE_ERR_SHAPE

@@ -569,3 +569,43 @@ def test_hip_graph_capture_replays_bitwise(name):
         assert torch.equal(r_out, want[2]) and torch.equal(xn, want[3]), f"replay {rep}: residual"
         layer.forward(x_other, y_other)     # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_empty_batch_through_every_entry_point():
+    """T = 0: moe_route and a routing output receive all-zero counts and
+    offsets (over a garbage prefill); the layer, the fused residual path, the
+    dense FFN and the residual norm write nothing and return MOE_OK."""
+    print("case empty batch T=0", flush=True)
+    g = _small(118, 4, 256, 16, 4, 64, 64)
+    E, K, H = 16, 4, 256
+    x0 = g["x"][:0]
+    r = B.route(x0, g["Wr"], g["b"], K, I=64, Is=64)
+    torch.cuda.synchronize()
+    assert r["topk_idx"].shape == (0, K)
+    assert int(r["counts"].abs().sum()) == 0 and int(r["offsets"].abs().sum()) == 0
+    out = B.alloc_routing(0, E, K, DEV)
+    out["counts"].fill_(7)
+    out["offsets"].fill_(-3)
+    B.route(x0, g["Wr"], g["b"], K, I=64, Is=64, out=out)
+    torch.cuda.synchronize()
+    assert (out["counts"].cpu() == 0).all() and (out["offsets"].cpu() == 0).all()
+
+    layer = B.MoELayer(g["Wr"], g["b"], g["wg"], g["wu"], g["wd"], g["sg"], g["su"], g["sd"], K=K)
+    rt = B.alloc_routing(0, E, K, DEV)
+    rt["counts"].fill_(5)
+    rt["offsets"].fill_(5)
+    y = layer.forward(x0, routing=rt)
+    torch.cuda.synchronize()
+    assert y.shape == (0, H)
+    assert (rt["counts"].cpu() == 0).all() and (rt["offsets"].cpu() == 0).all()
+    r_out = layer.forward_residual(x0, torch.empty((0, H), dtype=torch.bfloat16, device=DEV))
+    assert r_out.shape == (0, H)
+    # a non-empty call after the empty ones is unaffected
+    _check_case(g, K)
+
+    dense = B.DenseFFN(g["wg"][0], g["wu"][0], g["wd"][0], S=1)
+    assert dense.forward(x0).shape == (0, H)
+    ro, xo = B.residual_rmsnorm(torch.empty((0, H), dtype=torch.bfloat16, device=DEV),
+                                torch.empty((0, H), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert ro.shape == (0, H) and xo.shape == (0, H)
