@@ -90,6 +90,9 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "dispatch_blocks_ragged": (115, 1500, 256, 16, 4, 128, 64),
     "dispatch_blocks_E1024": (116, 1300, 256, 1024, 16, 64, 64),
     "wide_router_E100": (117, 1100, 2048, 100, 6, 128, 128),
+    "max_H_lds": (119, 400, 16384, 8, 2, 128, 128),
+    "max_I_lds": (120, 400, 256, 8, 2, 16384, 128),
+    "max_I_Is_decode": (122, 12, 256, 8, 2, 16384, 16384),
 }
 
 
@@ -136,6 +139,27 @@ def test_deterministic_and_permutation_equivariant():
     y3, r3, _ = _run(gp, 4)
     assert np.array_equal(y3, y1[p.numpy()])
     assert np.array_equal(r3["topk_idx"], r1["topk_idx"][p.numpy()])
+
+
+def test_max_tokens_sampled():
+    """T = 2^20, the largest batch the ABI takes (H=256, E=16, K=2, I=Is=128:
+    the 256-token router tiles, the three-kernel dispatch over 4096 blocks,
+    ~131k rows per expert in the LDS kernels).  Routing is checked on every
+    token, the output on 512 sampled rows."""
+    T, H, E, K, I, Is = 1 << 20, 256, 16, 2, 128, 128
+    print(f"case max tokens T={T} H={H} E={E} K={K} I={I} Is={Is}", flush=True)
+    g = _small(121, T, H, E, K, I, Is)
+    y, rg, _ = _run(g, K)
+    x64 = host_f64(g["x"])
+    Wr, b = host_f64(g["Wr"]), host_f64(g["b"])
+    check_routing(rg, oracle.route(x64, Wr, b, K), K, E, b)
+    rng = np.random.default_rng(121)
+    rows = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 510, replace=False)]))
+    yref = oracle.moe_layer(x64[rows], Wr, b, host_f64(g["wg"]), host_f64(g["wu"]),
+                            host_f64(g["wd"]), host_f64(g["sg"]), host_f64(g["su"]),
+                            host_f64(g["sd"]), K=K, sel=rg["topk_idx"].astype(np.int64)[rows])
+    res = check_output(y[rows], yref)
+    print(f"  rows={len(rows)} max_rel={res[0]:.3e} l2_rel={res[1]:.3e}", flush=True)
 
 
 # ---------------------------------------------------------------- Flash shape
