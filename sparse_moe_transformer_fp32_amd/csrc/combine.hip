@@ -24,6 +24,20 @@ __device__ inline uint32_t pack2(float a, float b) {
          ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+// The K slot rows of token t, then their 8 columns at c: all loads issued
+// before the first add (K <= 16, uniform), so a thread waits for one memory
+// latency instead of K.
+__device__ inline void load_slots(const uint16_t* __restrict__ o,
+                                  const int32_t* __restrict__ slot_pos, int t, int K, int H,
+                                  int c, u32x4 (&v)[16]) {
+  int rows[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) rows[j] = j < K ? slot_pos[(size_t)t * K + j] : 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    if (j < K) v[j] = *reinterpret_cast<const u32x4*>(o + (size_t)rows[j] * H + c);
+}
+
 // y[t] = sum_j o[slot_pos[t,j]] + o[KT + t]: rows already carry their
 // weights.  fp32 sum in slot order, shared expert last, one rounding.  No
 // atomics: each thread owns 8 columns of one token.
@@ -37,13 +51,16 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  for (int j = 0; j < K; ++j) {
-    const int row = slot_pos[(size_t)t * K + j];
-    const u32x4 v = *reinterpret_cast<const u32x4*>(o + (size_t)row * H + c);
-    float f[8];
-    bf16x8_to_f32(v, f);
+  u32x4 v[16];
+  load_slots(o, slot_pos, t, K, H, c, v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += f[i];
+  for (int j = 0; j < 16; ++j) {
+    if (j < K) {
+      float f[8];
+      bf16x8_to_f32(v[j], f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += f[i];
+    }
   }
   if (has_shared) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(o + (size_t)(KT + t) * H + c);
@@ -100,6 +117,8 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = 0.f;
       if (FUSED) {
+        // (one row at a time: this kernel keeps the whole row for the norm,
+        // and holding all K slot vectors as well halves its occupancy)
         add = true;
         for (int j = 0; j < a.K; ++j) {
           const int row = a.slot_pos[(size_t)t * a.K + j];
