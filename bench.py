@@ -401,6 +401,41 @@ def cpu_baseline(res, max_tokens=16, budget_s=10.0):
                       f"BLAS threads = {cores}"}
 
 
+def library_reference(reps=10):
+    """The vendor library on the same math, for context: torch.bmm (hipBLASLt)
+    of bf16 [E, M, K] x [E, K, N], contiguous operands, with M the mean rows
+    per expert of the prefill (114), 8192-token (228) and long (910)
+    workloads, for the gate/up (K=4096, N=2560) and down (K=1280, N=4096)
+    shapes; no gather, no activation, no routing.  Plus one dense GEMM
+    32768 x 4096 x 2560."""
+    import torch
+    out = []
+    shapes = []
+    for m in (114, 228, 910):
+        shapes += [(288, m, 4096, 2560, "gate_up"), (288, m, 1280, 4096, "down")]
+    shapes.append((1, 32768, 4096, 2560, "dense"))
+    for E, M, K, N, what in shapes:
+        a = torch.randn(E, M, K, device="cuda", dtype=torch.bfloat16)
+        b = torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16).contiguous()
+        c = torch.empty(E, M, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.bmm(a, b, out=c)
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            torch.bmm(a, b, out=c)
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / reps
+        tf = 2.0 * E * M * K * N / ms / 1e9
+        out.append({"shape": what, "E": E, "M": M, "K": K, "N": N, "ms": round(ms, 4),
+                    "tflops": round(tf, 1), "mfma_frac": round(tf / MFMA_BF16_PEAK_TFLOPS, 4)})
+        del a, b, c
+        torch.cuda.empty_cache()
+    return out
+
+
 def roofline_obj(bound, achieved, peak, unit, traffic):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -419,6 +454,9 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the "
                          "known-size reference for HBM byte counters) and exit")
+    ap.add_argument("--library-reference", action="store_true",
+                    help="only time torch.bmm (the vendor GEMM library) on the grouped "
+                         "GEMM shapes, for context, and exit")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-FFN side measurements of the default run")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG",
@@ -447,6 +485,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 1 << 30, "copies": 3}))
+        return
+    if args.library_reference:
+        print(json.dumps({"library_reference": library_reference()}), flush=True)
         return
     if args.workload.startswith("dense"):
         d = run_dense_bench(args.workload, args.steps, args.warmup)

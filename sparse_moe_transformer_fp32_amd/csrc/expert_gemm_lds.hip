@@ -43,6 +43,9 @@
 //  - The number of 32-token fragments with real rows (NA) is a template
 //    argument, so the MFMA stream has no branches, and the waves gather only
 //    those fragments' rows (NA loads per wave per stage).
+//  - The epilogue (SwiGLU for gate/up, the routing weight for down) stages
+//    the output tile in LDS, in the token ring's memory, and writes whole
+//    rows with 16-byte non-temporal stores.
 //
 // XCD-aware order: block b runs on XCD b % 8.  Work items, ordered (group,
 // weight tile, row block), are dealt to the XCDs in chunks of 32 in turn.
@@ -286,19 +289,27 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   wait_vmcnt<0>();
 
   // epilogue: accumulator register j of a lane is weight row
-  // 8(j/4) + 4 hi + j%4 of the fragment, token row 32 n + l31
+  // 8(j/4) + 4 hi + j%4 of the fragment, token row 32 n + l31.  The tile's
+  // bf16 outputs go to LDS as [token][output column] rows (pitch padded by
+  // 16 bytes against bank conflicts); then every thread stores 16-byte
+  // chunks of whole rows, so a wave writes full cache lines instead of
+  // 16-byte pieces of 32 rows.  The stores are non-temporal: h and o are
+  // read once, by the next kernel, and need not displace weights and token
+  // rows from L2.
+  constexpr int kOut = (MODE == 0) ? 64 * kFR : 128 * kFR;   // output columns of the tile
+  constexpr int kPitch = kOut * 2 + 16;                     // bytes per staged row
+  constexpr int kCPR = kOut / 8;                            // 16-byte chunks per row
+  unsigned char* stg = &ring[0][0];
+  __syncthreads();   // every wave is done with the ring
 #pragma unroll
   for (int n = 0; n < NA; ++n) {
     const int R = 32 * n + l31;
-    if (R >= blk.n_rows) continue;
-    const int row = blk.row_start + R;
+    unsigned char* srow = stg + R * kPitch;
     if (MODE == 0) {
       const float lim = shared ? P.limit_shared : P.limit;
-      uint16_t* hrow = shared ? P.out + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
-                              : P.out + (size_t)row * P.I;
 #pragma unroll
       for (int f = 0; f < kFR; ++f) {
-        const int cb = col0 + wave * 16 * kFR + 16 * f;   // first column of fragment f
+        const int lc = wave * 16 * kFR + 16 * f;   // tile column of fragment f
         float hv[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -315,30 +326,48 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
         p0[1] = pack_bf16x2_l(hv[2], hv[3]);
         p1[0] = pack_bf16x2_l(hv[4], hv[5]);
         p1[1] = pack_bf16x2_l(hv[6], hv[7]);
-        *reinterpret_cast<u32x2*>(hrow + cb + 4 * hi) = p0;
-        *reinterpret_cast<u32x2*>(hrow + cb + 8 + 4 * hi) = p1;
+        *reinterpret_cast<u32x2*>(srow + 2 * (lc + 4 * hi)) = p0;
+        *reinterpret_cast<u32x2*>(srow + 2 * (lc + 8 + 4 * hi)) = p1;
       }
     } else {
-      const float wr = P.row_w[row];
-      uint16_t* orow = P.out + (size_t)row * P.H;
+      const float wr = R < blk.n_rows ? P.row_w[blk.row_start + R] : 0.f;
 #pragma unroll
       for (int f = 0; f < kFR; ++f) {
-        const int rb0 = col0 + wave * 32 * kFR + 32 * f;   // first output row of fragment f
+        const int lr = wave * 32 * kFR + 32 * f;   // tile column (output row) of fragment f
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           u32x2 pk;
           pk[0] = pack_bf16x2_l(acc[f][n][4 * jj] * wr, acc[f][n][4 * jj + 1] * wr);
           pk[1] = pack_bf16x2_l(acc[f][n][4 * jj + 2] * wr, acc[f][n][4 * jj + 3] * wr);
-          *reinterpret_cast<u32x2*>(orow + rb0 + 8 * jj + 4 * hi) = pk;
+          *reinterpret_cast<u32x2*>(srow + 2 * (lr + 8 * jj + 4 * hi)) = pk;
         }
       }
     }
+  }
+  __syncthreads();
+  // rows past the block's end stay in LDS
+  const int n_chunks = blk.n_rows * kCPR;
+  for (int q = threadIdx.x; q < n_chunks; q += 256) {
+    const int R = q / kCPR, c = q % kCPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stg + R * kPitch + 16 * c);
+    const int row = blk.row_start + R;
+    uint16_t* dst;
+    if (MODE == 0)
+      dst = (shared ? P.out + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
+                    : P.out + (size_t)row * P.I) + col0 + 8 * c;
+    else
+      dst = P.out + (size_t)row * P.H + col0 + 8 * c;
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
   }
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
-  __shared__ __attribute__((aligned(1024))) unsigned char ring[kTSlots][kStage];
+  // the token ring during the K loop, then the output tile of the epilogue
+  constexpr int kStg = kRows * (((MODE == 0) ? 64 * kFR : 128 * kFR) * 2 + 16);
+  constexpr int kLds = kStg > kTSlots * kStage ? kStg : kTSlots * kStage;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
+  auto ring = reinterpret_cast<unsigned char (*)[kStage]>(lds);
 
   // XCD-aware deal of work items, ordered (group, weight tile, row block):
   // the items are cut in chunks of kChunk, dealt to the 8 XCDs in turn, so
