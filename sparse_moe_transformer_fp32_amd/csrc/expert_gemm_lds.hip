@@ -13,15 +13,17 @@
 // holds row 8(j/4) + 4(l/32) + j%4 of column l%32.
 //
 // Workgroup tile: 256 weight rows x one row block of up to 192 tokens.  Each
-// of the 4 waves owns two 32-row weight fragments and multiplies them with
-// every 32-token fragment of the block (12 accumulator tiles), so each
-// weight element is read from memory once per row block.  For gate/up a
+// of the 8 waves (two per SIMD) owns one 32-row weight fragment and
+// multiplies it with every 32-token fragment of the block (6 accumulator
+// tiles, 96 registers), so each weight element is read from memory once per
+// row block, and while one wave of a SIMD waits for memory the other can
+// issue MFMAs.  For gate/up a
 // weight fragment is 16 gate rows over 16 up rows of the same intermediate
 // columns, so accumulator registers j and j+8 of a lane are the gate and up
 // values of one output and SwiGLU happens in registers.
 //
 // Pipeline, one 64-wide k stage per step:
-//  - Tokens (shared by the 4 waves) are gathered with full-line loads: one
+//  - Tokens (shared by the 8 waves) are gathered with full-line loads: one
 //    load instruction moves 8 rows x 128 bytes (8 lanes per row) into
 //    registers, and two stages later the wave writes them to a 2-slot LDS
 //    ring, lane l's 16 bytes at row-group base + 16 l.  The global side
@@ -42,7 +44,7 @@
 //    that last chunk's MFMAs.
 //  - The number of 32-token fragments with real rows (NA) is a template
 //    argument, so the MFMA stream has no branches, and the waves gather only
-//    those fragments' rows (NA loads per wave per stage).
+//    those fragments' rows (ceil(NA/2) loads per wave per stage).
 //  - The epilogue (SwiGLU for gate/up, the routing weight for down) stages
 //    the output tile in LDS, in the token ring's memory, and writes whole
 //    rows with 16-byte non-temporal stores.
@@ -79,7 +81,8 @@ struct LdsGemmParams {
 namespace {
 
 constexpr int kRows = 192;            // token rows per row block at most (the plan's bn)
-constexpr int kFR = 2;                // 32-row weight fragments per wave
+constexpr int kFR = 1;                // 32-row weight fragments per wave
+constexpr int kWaves = 8;             // waves per workgroup: 8 x 32 = 256 weight rows
 constexpr int kKC = 4;                // 16-wide k chunks per 64-wide stage
 constexpr int kStage = kRows * 128;   // token bytes per stage
 constexpr int kWSlots = 3;            // weight register ring slots
@@ -119,9 +122,10 @@ template <int MODE, int NA>
 __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowBlock& blk,
                                               bool shared, int col0, int nst,
                                               unsigned char (*ring)[kStage]) {
-  // token loads per wave per stage (8 rows each): the 4 waves bring the
-  // 32 NA rows of the fragments in use
-  constexpr int kTL = NA;
+  // token loads per wave per stage (8 rows each): the 8 waves bring the
+  // 32 NA rows of the fragments in use (for odd NA the last loads repeat the
+  // block's last row into LDS rows no fragment reads)
+  constexpr int kTL = (NA * 4 + kWaves - 1) / kWaves;
   constexpr int kLoads = kFR * kKC + kTL;   // vector-memory ops per wave per stage
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -296,7 +300,7 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   // 16-byte pieces of 32 rows.  The stores are non-temporal: h and o are
   // read once, by the next kernel, and need not displace weights and token
   // rows from L2.
-  constexpr int kOut = (MODE == 0) ? 64 * kFR : 128 * kFR;   // output columns of the tile
+  constexpr int kOut = ((MODE == 0) ? 16 : 32) * kFR * kWaves;   // output columns of the tile
   constexpr int kPitch = kOut * 2 + 16;                     // bytes per staged row
   constexpr int kCPR = kOut / 8;                            // 16-byte chunks per row
   unsigned char* stg = &ring[0][0];
@@ -347,7 +351,7 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   __syncthreads();
   // rows past the block's end stay in LDS
   const int n_chunks = blk.n_rows * kCPR;
-  for (int q = threadIdx.x; q < n_chunks; q += 256) {
+  for (int q = threadIdx.x; q < n_chunks; q += 64 * kWaves) {
     const int R = q / kCPR, c = q % kCPR;
     const u32x4 v = *reinterpret_cast<const u32x4*>(stg + R * kPitch + 16 * c);
     const int row = blk.row_start + R;
@@ -362,9 +366,9 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
 }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void expert_gemm_lds_kernel(LdsGemmParams P) {
+__global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmParams P) {
   // the token ring during the K loop, then the output tile of the epilogue
-  constexpr int kStg = kRows * (((MODE == 0) ? 64 * kFR : 128 * kFR) * 2 + 16);
+  constexpr int kStg = kRows * (((MODE == 0) ? 16 : 32) * kFR * kWaves * 2 + 16);
   constexpr int kLds = kStg > kTSlots * kStage ? kStg : kTSlots * kStage;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
   auto ring = reinterpret_cast<unsigned char (*)[kStage]>(lds);
@@ -416,7 +420,7 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
   gp.row_token = a.row_token; gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.h;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.gu_tiles;
   gp.limit = a.limit; gp.limit_shared = a.limit_shared;
-  hipLaunchKernelGGL(expert_gemm_lds_kernel<0>, dim3(lds_grid(p, p.gu_tiles)), dim3(256), 0, s,
+  hipLaunchKernelGGL(expert_gemm_lds_kernel<0>, dim3(lds_grid(p, p.gu_tiles)), dim3(64 * kWaves), 0, s,
                      gp);
   return hipGetLastError();
 }
@@ -427,7 +431,7 @@ hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
   gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.o;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.dn_tiles;
-  hipLaunchKernelGGL(expert_gemm_lds_kernel<1>, dim3(lds_grid(p, p.dn_tiles)), dim3(256), 0, s,
+  hipLaunchKernelGGL(expert_gemm_lds_kernel<1>, dim3(lds_grid(p, p.dn_tiles)), dim3(64 * kWaves), 0, s,
                      gp);
   return hipGetLastError();
 }
