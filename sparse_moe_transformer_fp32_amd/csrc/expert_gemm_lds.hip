@@ -25,7 +25,7 @@
 // Pipeline, one 64-wide k stage per step:
 //  - Tokens (shared by the 8 waves) are gathered with full-line loads: one
 //    load instruction moves 8 rows x 128 bytes (8 lanes per row) into
-//    registers, and two stages later the wave writes them to a 2-slot LDS
+//    registers, and one stage later the wave writes them to a 2-slot LDS
 //    ring, lane l's 16 bytes at row-group base + 16 l.  The global side
 //    fetches chunk (l%8) ^ s(row) of its row, s(row) = (row/2) % 8: the
 //    swizzle spreads the rows of every 8-lane read group over distinct LDS
@@ -36,8 +36,8 @@
 //  - Weights are used by one wave only and skip LDS: packed tiles go straight
 //    into a 3-slot register ring.  One 64-wide stage of a packed 16-row tile
 //    is 1024 contiguous elements.
-//  - Stage s issues the weights of stage s+2 and the tokens of stage s+3,
-//    multiplies its four k chunks
+//  - Stage s issues the weights and the tokens of stage s+2, multiplies its
+//    four k chunks
 //    (the LDS reads of chunk q+1 in flight under the MFMAs of chunk q), and
 //    before its last chunk stores stage s+1's tokens to LDS and meets the
 //    other waves at a barrier, so the first chunk of stage s+1 is read under
@@ -219,23 +219,22 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   };
 
   u32x4 w[kWSlots][kFR][kKC];   // weights of stages s, s+1, s+2
-  u32x4 ts[3][kTL];              // tokens of stages s+1..s+3 on their way to LDS
+  u32x4 ts[2][kTL];              // tokens of stages s+1, s+2 on their way to LDS
   u32x4 t[2][NA];                // B operands of the current and the next k chunk
-  // Stage s (weight slot s%3, token staging buffer s%3, LDS slot s%2) first
-  // issues the weights of stage s+2 and the tokens of stage s+3.  Stage s+1's
-  // tokens were loaded two stages ago; all loads go to registers and
-  // complete in order, so vmcnt(2*kLoads) leaves only the two younger
-  // stages' loads in flight and they have arrived.  They go to LDS slot
-  // (s+1)%2, last read in stage s-1 (every wave finished those reads before
-  // the barrier of stage s-1, which all waves have passed).  The barrier
-  // after lgkmcnt(0) publishes them for the first chunk of s+1.
-  auto stage = [&](auto wc, auto sc, auto tc, int s) {
+  // Stage s (weight slot s%3, token staging buffer and LDS slot s%2) first
+  // issues the weights and the tokens of stage s+2.  Stage s+1's tokens were
+  // loaded one stage ago; all loads go to registers and complete in order,
+  // so vmcnt(kLoads) leaves only this stage's loads in flight and they have
+  // arrived.  They go to LDS slot (s+1)%2, last read in stage s-1 (every
+  // wave finished those reads before the barrier of stage s-1, which all
+  // waves have passed).  The barrier after lgkmcnt(0) publishes them for the
+  // first chunk of s+1.
+  auto stage = [&](auto wc, auto tc, int s) {
     constexpr int jw = decltype(wc)::value;   // s % 3
-    constexpr int js = decltype(sc)::value;   // s % 3 (staging buffer of stage s+3)
     constexpr int jt = decltype(tc)::value;   // s % 2
-    constexpr int jw2 = (jw + 2) % kWSlots, js1 = (js + 1) % 3, jt1 = (jt + 1) % kTSlots;
+    constexpr int jw2 = (jw + 2) % kWSlots, jt1 = (jt + 1) % kTSlots;
     load_w(w[jw2], s + 2);
-    load_t(ts[js], s + 3);
+    load_t(ts[jt], s + 2);
     __builtin_amdgcn_sched_barrier(0);
     read_t(ring[jt], 1, t[1]);
     __builtin_amdgcn_sched_barrier(0);
@@ -249,8 +248,8 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     __builtin_amdgcn_sched_barrier(0);
     mma(w[jw], 2, t[0]);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<2 * kLoads>();
-    write_t(ring[jt1], ts[js1]);
+    wait_vmcnt<kLoads>();
+    write_t(ring[jt1], ts[jt1]);
     wait_lds();
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
@@ -260,36 +259,34 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue in the same issue pattern: T0, then (W0, T1) and (W1, T2) as
-  // stages -2 and -1 would issue them
-  load_t(ts[0], 0);
+  // prologue in the same issue pattern: (W0, T0) and (W1, T1) as stages -2
+  // and -1 would issue them
   load_w(w[0], 0);
-  load_t(ts[1], 1);
+  load_t(ts[0], 0);
   load_w(w[1], 1);
-  load_t(ts[2], 2);
+  load_t(ts[1], 1);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<2 * kLoads>();   // stage 0's tokens have arrived
+  wait_vmcnt<kLoads>();   // stage 0's tokens have arrived
   write_t(ring[0], ts[0]);
   wait_lds();
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read_t(ring[0], 0, t[0]);
-  // stage s stages tokens of s+3 in buffer s%3 (buffer (s+3)%3 = s%3)
   int s = 0;
   for (; s + 6 <= nst; s += 6) {
-    stage(ic<0>{}, ic<0>{}, ic<0>{}, s);
-    stage(ic<1>{}, ic<1>{}, ic<1>{}, s + 1);
-    stage(ic<2>{}, ic<2>{}, ic<0>{}, s + 2);
-    stage(ic<0>{}, ic<0>{}, ic<1>{}, s + 3);
-    stage(ic<1>{}, ic<1>{}, ic<0>{}, s + 4);
-    stage(ic<2>{}, ic<2>{}, ic<1>{}, s + 5);
+    stage(ic<0>{}, ic<0>{}, s);
+    stage(ic<1>{}, ic<1>{}, s + 1);
+    stage(ic<2>{}, ic<0>{}, s + 2);
+    stage(ic<0>{}, ic<1>{}, s + 3);
+    stage(ic<1>{}, ic<0>{}, s + 4);
+    stage(ic<2>{}, ic<1>{}, s + 5);
   }
   // tail: the remaining stages continue the same slot sequence
-  if (s < nst) stage(ic<0>{}, ic<0>{}, ic<0>{}, s);
-  if (s + 1 < nst) stage(ic<1>{}, ic<1>{}, ic<1>{}, s + 1);
-  if (s + 2 < nst) stage(ic<2>{}, ic<2>{}, ic<0>{}, s + 2);
-  if (s + 3 < nst) stage(ic<0>{}, ic<0>{}, ic<1>{}, s + 3);
-  if (s + 4 < nst) stage(ic<1>{}, ic<1>{}, ic<0>{}, s + 4);
+  if (s < nst) stage(ic<0>{}, ic<0>{}, s);
+  if (s + 1 < nst) stage(ic<1>{}, ic<1>{}, s + 1);
+  if (s + 2 < nst) stage(ic<2>{}, ic<0>{}, s + 2);
+  if (s + 3 < nst) stage(ic<0>{}, ic<1>{}, s + 3);
+  if (s + 4 < nst) stage(ic<1>{}, ic<0>{}, s + 4);
   wait_vmcnt<0>();
 
   // epilogue: accumulator register j of a lane is weight row
