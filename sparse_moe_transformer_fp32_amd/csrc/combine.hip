@@ -26,7 +26,9 @@ __device__ inline uint32_t pack2(float a, float b) {
 
 // The K slot rows of token t, then their 8 columns at c: all loads issued
 // before the first add (K <= 16, uniform), so a thread waits for one memory
-// latency instead of K.
+// latency instead of K.  Every expert row is read once, here: the loads are
+// non-temporal (they stream from HBM faster than ordinary loads).  The same
+// holds for the fused kernel's expert rows and residual input.
 __device__ inline void load_slots(const uint16_t* __restrict__ o,
                                   const int32_t* __restrict__ slot_pos, int t, int K, int H,
                                   int c, u32x4 (&v)[16]) {
@@ -35,7 +37,7 @@ __device__ inline void load_slots(const uint16_t* __restrict__ o,
   for (int j = 0; j < 16; ++j) rows[j] = j < K ? slot_pos[(size_t)t * K + j] : 0;
 #pragma unroll
   for (int j = 0; j < 16; ++j)
-    if (j < K) v[j] = *reinterpret_cast<const u32x4*>(o + (size_t)rows[j] * H + c);
+    if (j < K) v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + (size_t)rows[j] * H + c));
 }
 
 // y[t] = sum_j o[slot_pos[t,j]] + o[KT + t]: rows already carry their
@@ -63,7 +65,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
     }
   }
   if (has_shared) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(o + (size_t)(KT + t) * H + c);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(o + (size_t)(KT + t) * H + c));
     float f[8];
     bf16x8_to_f32(v, f);
 #pragma unroll
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
   for (int ch = 0; ch < 8; ++ch) {
     const int c = (ch * 256 + threadIdx.x) * 8;
     if (c < H) {
-      const u32x4 rin = *reinterpret_cast<const u32x4*>(a.r_in + (size_t)t * H + c);
+      const u32x4 rin = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r_in + (size_t)t * H + c));
       float f[8];
       bf16x8_to_f32(rin, f);
       bool add = false;
@@ -123,13 +125,13 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
         for (int j = 0; j < a.K; ++j) {
           const int row = a.slot_pos[(size_t)t * a.K + j];
           float fo[8];
-          bf16x8_to_f32(*reinterpret_cast<const u32x4*>(a.o + (size_t)row * H + c), fo);
+          bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.o + (size_t)row * H + c)), fo);
 #pragma unroll
           for (int i = 0; i < 8; ++i) y[i] += fo[i];
         }
         if (a.has_shared) {
           float fo[8];
-          bf16x8_to_f32(*reinterpret_cast<const u32x4*>(a.o + (size_t)(a.KT + t) * H + c), fo);
+          bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.o + (size_t)(a.KT + t) * H + c)), fo);
 #pragma unroll
           for (int i = 0; i < 8; ++i) y[i] += fo[i];
         }

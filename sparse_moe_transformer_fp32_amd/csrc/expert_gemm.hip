@@ -16,7 +16,8 @@
 // contiguous kilobyte.  The
 // token rows (B operand) are small and hot in L2.  A wave owns FR fragments
 // of 16 weight rows and all 16*NB rows of its row block; KSPLIT waves of a
-// workgroup split K and add their partial sums in a fixed order through LDS
+// workgroup split K (interleaved k steps) and add their partial sums in a
+// fixed order through LDS
 // (so small-T launches have enough, small enough workgroups to balance the
 // weight stream over the CUs).
 //
@@ -55,23 +56,21 @@ __device__ inline f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// MODE 0: gate/up + SwiGLU.  MODE 1: down + combine weight.
-template <int MODE, int NB, int FR, int KSPLIT, int U>
-__global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
+template <int KSPLIT, int FR, int NB>
+constexpr int red_slots() { return ((KSPLIT > 1) ? (4 - 4 / KSPLIT) : 1) * FR * NB * 64; }
+
+// One workgroup's tile of one row block.  MODE 0: gate/up + SwiGLU.  MODE 1:
+// down + combine weight.  NT: the weight loads are non-temporal.
+template <int MODE, int NB, int FR, int KSPLIT, int U, bool NT>
+__device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& blk, int tile,
+                                          f32x4* s_red) {
   constexpr int RG = 4 / KSPLIT;                       // row groups per workgroup
   constexpr int WROWS = (MODE == 0) ? 8 * FR : 16 * FR;  // output columns per wave
-  constexpr int NRED = (KSPLIT > 1) ? (4 - RG) : 1;
-  __shared__ f32x4 s_red[NRED * FR * NB * 64];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int rg = wave / KSPLIT, kp = wave % KSPLIT;
   const int r = lane & 15, g = lane >> 4;
-
-  const int tile = blockIdx.x % P.tiles;
-  const int rbi = blockIdx.x / P.tiles;
-  if (rbi >= *P.n_rb) return;
-  const RowBlock blk = P.rb[rbi];
   const bool shared = blk.group == P.E;
   const int inter = shared ? P.Is : P.I;
   const int nout = (MODE == 0) ? inter : P.H;          // output columns of this group
@@ -80,12 +79,16 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
   const int cbase = col0 + rg * WROWS;                 // this wave's first column
   const int Kdim = (MODE == 0) ? P.H : inter;
   const int klen = Kdim / KSPLIT;
-  const int kbeg = kp * klen + 8 * g;
+  const int kbeg = kp * 32 + 8 * g;
 
   // A operand: fragment-packed weights (16x32 tiles of 1 KB in lane order,
-  // row-tile-major); this wave walks K inside its row tiles
+  // row-tile-major).  The KSPLIT waves of a row group take every KSPLIT-th
+  // 32-wide k step, so together they read each row tile's kilobytes front to
+  // back: one sequential stream per row tile and workgroup.  (Contiguous K
+  // quarters per wave made four streams 32 KB apart; a plain read kernel
+  // with that pattern reaches ~6.0 TB/s, with the interleaved one ~7.0.)
   const int ksteps = Kdim / 32;
-  const int kstep0 = kp * (klen / 32);
+  const int kstep0 = kp;
   const uint16_t* aptr[FR];
   if (MODE == 0) {
     const uint16_t* Wg = shared ? P.sa0 : P.wa0 + (size_t)blk.group * P.I * P.H;
@@ -126,7 +129,8 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
   // Software pipeline over stages of U k-steps with two register buffers.
   // Every load is unconditional so the compiler's wait counts let one stage
   // stream in while the other is multiplied; slots past the end of K re-read
-  // the last valid chunk (in bounds) and skip their MFMAs.
+  // the last valid chunk (in bounds) and skip their MFMAs.  Token rows,
+  // re-read by every workgroup of their row block, are ordinary loads.
   const int nsteps = klen / 32;
   const int nstages = (nsteps + U - 1) / U;
   u32x4 a0[U][FR], b0[U][NB], a1[U][FR], b1[U][NB];
@@ -135,10 +139,13 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
     for (int u = 0; u < U; ++u) {
       const int ks = min(stage * U + u, nsteps - 1);
 #pragma unroll
-      for (int f = 0; f < FR; ++f) a[u][f] = *reinterpret_cast<const u32x4*>(aptr[f] + ks * 512);
+      for (int f = 0; f < FR; ++f) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(aptr[f] + (size_t)ks * (KSPLIT * 512));
+        a[u][f] = NT ? __builtin_nontemporal_load(src) : *src;
+      }
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + ks * 32);
+        b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + ks * (KSPLIT * 32));
     }
   };
   auto compute = [&](const u32x4 (&a)[U][FR], const u32x4 (&b)[U][NB], int stage) {
@@ -230,6 +237,27 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
       }
     }
   }
+}
+
+// The grid covers rb_max row blocks x tiles; workgroups past the list's end
+// exit.  A row block that is its group's only one is the single reader of
+// its weight tile, which then streams with non-temporal loads: they lift the
+// HBM read rate (a plain read kernel moves ~6.2 TB/s with ordinary loads and
+// ~7.0 TB/s with non-temporal ones).  Tiles that several row blocks read use
+// ordinary loads, so the blocks after the first find them in L2.
+template <int MODE, int NB, int FR, int KSPLIT, int U>
+__global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
+  __shared__ f32x4 s_red[red_slots<KSPLIT, FR, NB>()];
+  const int tile = blockIdx.x % P.tiles;
+  const int rbi = blockIdx.x / P.tiles;
+  // both loads at once: rbi < rb_max, so the entry is in bounds even past
+  // the list's end (where it is not used)
+  const RowBlock blk = P.rb[rbi];
+  if (rbi >= *P.n_rb) return;
+  if (blk.n_group == 1)
+    gemm_tile<MODE, NB, FR, KSPLIT, U, true>(P, blk, tile, s_red);
+  else
+    gemm_tile<MODE, NB, FR, KSPLIT, U, false>(P, blk, tile, s_red);
 }
 
 // --------------------------------------------------------------------------

@@ -118,7 +118,7 @@ using ic = std::integral_constant<int, I>;
 
 // The pipelined K loop and the epilogue for one work item whose row block
 // has NA 32-token fragments with real rows.
-template <int MODE, int NA>
+template <int MODE, int NA, bool NT>
 __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowBlock& blk,
                                               bool shared, int col0, int nst,
                                               unsigned char (*ring)[kStage]) {
@@ -191,7 +191,9 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     for (int f = 0; f < kFR; ++f)
 #pragma unroll
       for (int q = 0; q < kKC; ++q)
-        w[f][q] = *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
+        w[f][q] = NT ? __builtin_nontemporal_load(
+                           reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q))
+                     : *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
   };
   auto load_t = [&](u32x4 (&v)[kTL], int s) {
     const int off = min(s, nst - 1) * 64;
@@ -362,6 +364,21 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   }
 }
 
+// the item's body for its number of 32-token fragments with rows
+template <int MODE, bool NT>
+__device__ __forceinline__ void lds_gemm_fragments(const LdsGemmParams& P, const RowBlock& blk,
+                                                   bool shared, int col0, int nst,
+                                                   unsigned char (*ring)[kStage]) {
+  switch ((blk.n_rows + 31) >> 5) {
+    case 1: lds_gemm_item<MODE, 1, NT>(P, blk, shared, col0, nst, ring); break;
+    case 2: lds_gemm_item<MODE, 2, NT>(P, blk, shared, col0, nst, ring); break;
+    case 3: lds_gemm_item<MODE, 3, NT>(P, blk, shared, col0, nst, ring); break;
+    case 4: lds_gemm_item<MODE, 4, NT>(P, blk, shared, col0, nst, ring); break;
+    case 5: lds_gemm_item<MODE, 5, NT>(P, blk, shared, col0, nst, ring); break;
+    default: lds_gemm_item<MODE, 6, NT>(P, blk, shared, col0, nst, ring); break;
+  }
+}
+
 template <int MODE>
 __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmParams P) {
   // the token ring during the K loop, then the output tile of the epilogue
@@ -392,14 +409,14 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
   const int col0 = tile * (MODE == 0 ? 128 : 256);  // first output column of the workgroup
   if (col0 >= nout) return;                          // uniform over the workgroup
   const int nst = ((MODE == 0) ? P.H : inter) >> 6;  // 64-wide k stages
-  switch ((blk.n_rows + 31) >> 5) {                   // 32-token fragments with rows
-    case 1: lds_gemm_item<MODE, 1>(P, blk, shared, col0, nst, ring); break;
-    case 2: lds_gemm_item<MODE, 2>(P, blk, shared, col0, nst, ring); break;
-    case 3: lds_gemm_item<MODE, 3>(P, blk, shared, col0, nst, ring); break;
-    case 4: lds_gemm_item<MODE, 4>(P, blk, shared, col0, nst, ring); break;
-    case 5: lds_gemm_item<MODE, 5>(P, blk, shared, col0, nst, ring); break;
-    default: lds_gemm_item<MODE, 6>(P, blk, shared, col0, nst, ring); break;
-  }
+  // A row block that is its group's only one is the single reader of its
+  // weight tile, which then streams with non-temporal loads (a higher HBM
+  // read rate); tiles that several row blocks read use ordinary loads, so
+  // the blocks after the first find them in L2.
+  if (blk.n_group == 1)
+    lds_gemm_fragments<MODE, true>(P, blk, shared, col0, nst, ring);
+  else
+    lds_gemm_fragments<MODE, false>(P, blk, shared, col0, nst, ring);
 }
 
 // grid: every chunk of kChunk (row block, weight tile) items up to the
