@@ -207,6 +207,46 @@ def write_traffic(pmc_root, commands):
     print("\n".join(text))
 
 
+def summarize_mfma(root, command):
+    """From rocprofv3 --pmc runs <root>/<workload>/run_counter_collection.csv
+    (workload = prefill, long) over the LDS-pipelined GEMMs, the per-dispatch
+    MFMA work, MFMA busy fraction, shader clock and LDS bank conflicts."""
+    import collections
+    from sparse_moe_transformer_fp32_amd.inputs import WORKLOADS
+    lines = ["# MFMA and LDS counters of the LDS-pipelined grouped GEMMs (rocprofv3 --pmc, one pass per workload)",
+             "# command (workload = prefill | long):", f"#   {command}",
+             "# mean per dispatch. Derived columns:",
+             "#   MFMA FLOP  = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (executed, including padded token rows);",
+             "#   cycles     = GRBM_GUI_ACTIVE / 8 (the 8 XCDs each count); clock = cycles / kernel time;",
+             "#   MFMA busy  = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles).",
+             "# The kernel times are the same run's dispatch timestamps.",
+             f"{'workload':9s} {'kernel':8s} {'time_us':>8s} {'clock_GHz':>9s} {'MFMA_TFLOP':>10s} "
+             f"{'alg_TFLOP':>9s} {'pad':>5s} {'MFMA_busy':>9s} {'LDS_bank_conf':>13s} {'waves':>7s}"]
+    for wl_name in ("prefill", "long"):
+        wl = WORKLOADS[wl_name]
+        gu_alg = 2 * (wl.K * wl.T * 2 * wl.I * wl.H + wl.T * 2 * wl.Is * wl.H)
+        disp = collections.defaultdict(dict)
+        for r in _read_csv(os.path.join(root, wl_name, "run_counter_collection.csv")):
+            d = disp[(r["Kernel_Name"], r["Dispatch_Id"])]
+            d[r["Counter_Name"]] = float(r["Counter_Value"])
+            d["_ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        for tag, key, alg in (("gate_up", "expert_gemm_lds_kernel<0>", gu_alg),
+                              ("down", "expert_gemm_lds_kernel<1>", gu_alg / 2)):
+            ds = [d for (k, _), d in disp.items() if key in k]
+            if not ds:
+                continue
+            m = {c: sum(d[c] for d in ds) / len(ds) for c in ds[0]}
+            cycles = m["GRBM_GUI_ACTIVE"] / 8
+            t_us = m["_ns"] / 1e3
+            flop = m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            lines.append(f"{wl_name:9s} {tag:8s} {t_us:8.1f} {cycles / (t_us * 1e3):9.2f} {flop / 1e12:10.3f} "
+                         f"{alg / 1e12:9.3f} {flop / alg:5.2f} "
+                         f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (1024 * cycles):8.1f}% "
+                         f"{m['SQ_LDS_BANK_CONFLICT']:13.0f} {m['SQ_WAVES']:7.0f}")
+    print("\n".join(lines))
+    return lines
+
+
 def layer_work(wl, counts):
     """Algorithmic bytes and FLOPs of one layer call, and of its gate/up
     kernel, from the measured expert counts."""
@@ -464,12 +504,19 @@ def main():
                          "a rocprofv3 kernel_stats.csv (and of its kernel trace per launch shape)")
     ap.add_argument("--write-traffic", nargs="+", metavar="ARG",
                     help="offline: PMC_ROOT COMMAND... -> profiles/traffic.json")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_ROOT", "OUT", "COMMAND"),
+                    help="offline: MFMA/LDS counter runs (prefill, long) -> a short summary")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
         return
     if args.write_traffic:
         write_traffic(args.write_traffic[0], args.write_traffic[1:])
+        return
+    if args.summarize_mfma:
+        root, out, command = args.summarize_mfma
+        with open(out, "w") as f:
+            f.write("\n".join(summarize_mfma(root, command)) + "\n")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; --gpus must be 1.",

@@ -91,3 +91,33 @@ def test_traffic_record_goes_stale_with_its_sources(tmp_path, monkeypatch):
     src.write_text("kernel v2\n")
     assert bench._traffic("gate_up:decode") is None
     assert bench._traffic("gate_up:prefill") is None
+
+
+def test_summarize_mfma_derived_columns(tmp_path):
+    """MFMA work = MOPS x 512, clock = GRBM_GUI_ACTIVE / 8 over the dispatch
+    time, busy = MFMA busy cycles over 1024 SIMDs x cycles."""
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value", "Start_Timestamp",
+           "End_Timestamp"]
+    for wl in ("prefill", "long"):
+        (tmp_path / wl).mkdir()
+        rows = []
+        for disp, kern in ((1, "void smoe::expert_gemm_lds_kernel<0>(P)"),
+                           (2, "void smoe::expert_gemm_lds_kernel<1>(P)")):
+            cycles = 2_000_000                      # per XCD: 1 ms at 2 GHz
+            vals = {"GRBM_GUI_ACTIVE": 8 * cycles, "SQ_INSTS_VALU_MFMA_MOPS_BF16": 1e9 / 512,
+                    "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 1024 * cycles, "SQ_LDS_BANK_CONFLICT": 7,
+                    "SQ_WAVES": 64, "SQ_BUSY_CU_CYCLES": 1, "SQ_LDS_IDX_ACTIVE": 1,
+                    "SQ_WAVE_CYCLES": 1}
+            for c, v in vals.items():
+                rows.append([disp, kern, c, v, 0, 1_000_000])
+        _write_csv(tmp_path / wl / "run_counter_collection.csv", hdr, rows)
+    lines = bench.summarize_mfma(str(tmp_path), "the command")
+    assert "#   the command" in lines
+    data = [l.split() for l in lines if l.startswith(("prefill", "long"))]
+    assert len(data) == 4
+    for wl, kernel, t_us, clock, mfma_tf, alg_tf, pad, busy, conf, waves in data:
+        assert float(t_us) == 1000.0 and float(clock) == 2.0
+        assert float(mfma_tf) == 0.001 and busy == "25.0%" and conf == "7" and waves == "64"
+        w = WORKLOADS[wl]
+        alg = 2 * (w.K * w.T * 2 * w.I * w.H + w.T * 2 * w.Is * w.H) / (1 if kernel == "gate_up" else 2)
+        assert abs(float(alg_tf) - alg / 1e12) < 1e-3
