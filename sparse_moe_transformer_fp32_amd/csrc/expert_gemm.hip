@@ -84,9 +84,10 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
   // A operand: fragment-packed weights (16x32 tiles of 1 KB in lane order,
   // row-tile-major).  The KSPLIT waves of a row group take every KSPLIT-th
   // 32-wide k step, so together they read each row tile's kilobytes front to
-  // back: one sequential stream per row tile and workgroup.  (Contiguous K
-  // quarters per wave made four streams 32 KB apart; a plain read kernel
-  // with that pattern reaches ~6.0 TB/s, with the interleaved one ~7.0.)
+  // back: one sequential stream per row tile and workgroup.  (With
+  // non-temporal loads, a plain read kernel reaches ~6.0 TB/s when each of
+  // four waves reads its own contiguous quarter of a region, ~7.0 TB/s when
+  // the four interleave like this.)
   const int ksteps = Kdim / 32;
   const int kstep0 = kp;
   const uint16_t* aptr[FR];
