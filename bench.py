@@ -247,6 +247,32 @@ def summarize_mfma(root, command):
     return lines
 
 
+def read_ceiling(gib: int = 4, reps: int = 10):
+    """HBM read rate of one plain read of a `gib` GiB buffer (moe_read_probe,
+    two workgroups per CU, 16-byte loads), ordinary and non-temporal, timed
+    with HIP events over `reps` reads after two untimed ones: the practical
+    ceiling of a weight stream, next to the nominal 8 TB/s."""
+    import torch
+    from sparse_moe_transformer_fp32_amd import binding as B
+    buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = {"bytes": gib << 30}
+    for name, nt in (("ordinary", False), ("nontemporal", True)):
+        for _ in range(2):
+            B.read_probe(buf, sink, nt)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            B.read_probe(buf, sink, nt)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        out[name] = {"us_per_read": round(ms * 1e3, 1),
+                     "gbs": round((gib << 30) / (ms * 1e-3) / 1e9, 1)}
+    out["frac_of_8tbs"] = {k: round(out[k]["gbs"] / 8000.0, 3) for k in ("ordinary", "nontemporal")}
+    return out
+
+
 def layer_work(wl, counts):
     """Algorithmic bytes and FLOPs of one layer call, and of its gate/up
     kernel, from the measured expert counts."""
@@ -497,6 +523,9 @@ def main():
     ap.add_argument("--library-reference", action="store_true",
                     help="only time torch.bmm (the vendor GEMM library) on the grouped "
                          "GEMM shapes, for context, and exit")
+    ap.add_argument("--read-ceiling", action="store_true",
+                    help="only measure the HBM read rate of a plain 4 GiB read (moe_read_probe) "
+                         "with ordinary and with non-temporal loads, and exit")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-FFN side measurements of the default run")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG",
@@ -535,6 +564,9 @@ def main():
         return
     if args.library_reference:
         print(json.dumps({"library_reference": library_reference()}), flush=True)
+        return
+    if args.read_ceiling:
+        print(json.dumps({"read_ceiling": read_ceiling()}), flush=True)
         return
     if args.workload.startswith("dense"):
         d = run_dense_bench(args.workload, args.steps, args.warmup)

@@ -324,6 +324,19 @@ moe_status moe_expert_stats(const moe_dims* d, const int32_t* offsets, const uin
  * stop.  Returns MOE_ERR_SHAPE unless n_events == 2*MOE_N_STAGES. */
 moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events);
 
+/* Measurement aid, not part of the layer: reads `bytes` of device memory at
+ * `buf` once with 16-byte loads (`nontemporal` = 1: non-temporal loads, the
+ * kind the weight streams use; 0: ordinary loads), two 256-thread
+ * workgroups per CU in a grid-stride loop, enqueued on `stream`.  It gives
+ * the HBM read rate a plain stream reaches, the practical ceiling the GEMMs'
+ * weight streams are compared with.  `sink` (16 bytes, device) is written
+ * only in a case that does not occur, so the kernel moves no data but the
+ * reads.  Returns MOE_ERR_NULL, MOE_ERR_ALIGN (buf or sink not 16-byte
+ * aligned), MOE_ERR_SHAPE (bytes not a positive multiple of 16384),
+ * MOE_ERR_OPTION, or MOE_ERR_DEVICE (launch failed). */
+moe_status moe_read_probe(const void* buf, size_t bytes, int32_t nontemporal, void* sink,
+                          hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_E
 EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
             "moe_route", "moe_forward", "moe_forward_residual", "moe_residual_rmsnorm",
             "moe_set_stage_events", "moe_pack_weights", "moe_pack_weights_strided",
-            "moe_dense_workspace_bytes", "moe_dense_ffn", "moe_expert_stats"]
+            "moe_dense_workspace_bytes", "moe_dense_ffn", "moe_expert_stats", "moe_read_probe"]
 STAGES = ["route_logits", "route_topk", "dispatch", "gate_up", "down", "combine"]
 
 _vp = ctypes.c_void_p
@@ -119,6 +119,8 @@ def load() -> ctypes.CDLL:
     lib.moe_pack_weights.argtypes = [_vp, _vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _vp]
     lib.moe_set_stage_events.restype = ctypes.c_int
     lib.moe_set_stage_events.argtypes = [_vp, ctypes.c_int32]
+    lib.moe_read_probe.restype = ctypes.c_int
+    lib.moe_read_probe.argtypes = [_vp, ctypes.c_size_t, ctypes.c_int32, _vp, _vp]
     v = lib.moe_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH}: ABI version {v}, binding expects {ABI_VERSION}")
@@ -431,6 +433,16 @@ def set_stage_events(events_array) -> None:
         _check(lib.moe_set_stage_events(None, 0))
     else:
         _check(lib.moe_set_stage_events(ctypes.cast(events_array, _vp), len(events_array)))
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool) -> None:
+    """One plain read of `buf` (device, 16-byte aligned, a multiple of 16384
+    bytes) with ordinary or non-temporal 16-byte loads, on the current stream
+    (moe_read_probe): the HBM read ceiling the weight streams are measured
+    against.  `sink` is a 16-byte device tensor the kernel does not write."""
+    lib = load()
+    _check(lib.moe_read_probe(_vp(buf.data_ptr()), buf.numel() * buf.element_size(),
+                              1 if nontemporal else 0, _vp(sink.data_ptr()), _stream(buf.device)))
 
 
 def residual_rmsnorm(r_in: torch.Tensor, y_add: Optional[torch.Tensor] = None,

@@ -578,6 +578,23 @@ moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, 
                                   stream);
 }
 
+moe_status moe_read_probe(const void* buf, size_t bytes, int32_t nontemporal, void* sink,
+                          hipStream_t stream) {
+  if (!buf || !sink) return fail(MOE_ERR_NULL, "moe_read_probe: NULL buffer or sink");
+  if (misaligned(buf) || misaligned(sink))
+    return fail(MOE_ERR_ALIGN, "moe_read_probe: buf and sink must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16384)
+    return fail(MOE_ERR_SHAPE, "moe_read_probe: bytes=%zu must be a positive multiple of 16384",
+                bytes);
+  if (nontemporal != 0 && nontemporal != 1)
+    return fail(MOE_ERR_OPTION, "moe_read_probe: nontemporal must be 0 or 1");
+  moe_status st;
+  if ((st = launched(smoe::launch_read_probe(buf, bytes, nontemporal != 0, sink, stream),
+                     "read_probe")))
+    return st;
+  return ok();
+}
+
 moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events) {
   if (!events) {
     g_stage_events = nullptr;

@@ -106,6 +106,8 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s);
 
 // counts[0..E) = 0 and offsets[0..E] = 0 (the routing of an empty batch)
+hipError_t launch_read_probe(const void* buf, size_t bytes, bool nontemporal, void* sink,
+                             hipStream_t s);
 hipError_t launch_zero_counts(int32_t* counts, int32_t* offsets, int E, hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,

@@ -292,3 +292,16 @@ def test_empty_batch_host_paths():
     d = B.dims(*empty)
     assert lib.moe_expert_stats(ctypes.byref(d), _vp(A), _vp(A), _vp(A), None,
                                 None) == B.MOE_ERR_SHAPE
+
+
+def test_read_probe_checks():
+    """moe_read_probe rejects bad arguments on the host, before any HIP call."""
+    lib = B.load()
+    assert lib.moe_read_probe(None, 16384, 1, _vp(A), None) == B.MOE_ERR_NULL
+    assert lib.moe_read_probe(_vp(A), 16384, 1, None, None) == B.MOE_ERR_NULL
+    assert lib.moe_read_probe(_vp(A + 8), 16384, 1, _vp(A), None) == B.MOE_ERR_ALIGN
+    assert lib.moe_read_probe(_vp(A), 16384, 1, _vp(A + 4), None) == B.MOE_ERR_ALIGN
+    assert lib.moe_read_probe(_vp(A), 0, 1, _vp(A), None) == B.MOE_ERR_SHAPE
+    assert lib.moe_read_probe(_vp(A), 16384 + 16, 0, _vp(A), None) == B.MOE_ERR_SHAPE
+    assert "multiple of 16384" in B.last_error()
+    assert lib.moe_read_probe(_vp(A), 16384, 2, _vp(A), None) == B.MOE_ERR_OPTION

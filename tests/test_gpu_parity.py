@@ -635,3 +635,14 @@ def test_empty_batch_through_every_entry_point():
                                 torch.empty((0, H), dtype=torch.bfloat16, device=DEV))
     torch.cuda.synchronize()
     assert ro.shape == (0, H) and xo.shape == (0, H)
+
+
+def test_read_probe_reads_without_writing():
+    """The HBM read-ceiling probe runs both load kinds over a buffer and
+    leaves its sink untouched (its write condition never holds)."""
+    buf = torch.ones(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    for nt in (False, True):
+        B.read_probe(buf, sink, nt)
+    torch.cuda.synchronize()
+    assert int(sink.sum()) == 0
