@@ -249,9 +249,10 @@ def summarize_mfma(root, command):
 
 def read_ceiling(gib: int = 4, reps: int = 10):
     """HBM read rate of one plain read of a `gib` GiB buffer (moe_read_probe,
-    two workgroups per CU, 16-byte loads), ordinary and non-temporal, timed
-    with HIP events over `reps` reads after two untimed ones: the practical
-    ceiling of a weight stream, next to the nominal 8 TB/s."""
+    two workgroups per CU, 16-byte loads), ordinary and non-temporal: the best
+    of three groups of `reps` reads timed with HIP events, after two untimed
+    reads.  The practical ceiling of a weight stream, next to the nominal
+    8 TB/s."""
     import torch
     from sparse_moe_transformer_fp32_amd import binding as B
     buf = torch.ones(gib << 30, dtype=torch.uint8, device="cuda")
@@ -260,15 +261,18 @@ def read_ceiling(gib: int = 4, reps: int = 10):
     for name, nt in (("ordinary", False), ("nontemporal", True)):
         for _ in range(2):
             B.read_probe(buf, sink, nt)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            B.read_probe(buf, sink, nt)
-        b.record()
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        out[name] = {"us_per_read": round(ms * 1e3, 1),
-                     "gbs": round((gib << 30) / (ms * 1e-3) / 1e9, 1)}
+        best = None
+        for _ in range(3):   # the best of three timed groups
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(reps):
+                B.read_probe(buf, sink, nt)
+            b.record()
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / reps
+            best = ms if best is None else min(best, ms)
+        out[name] = {"us_per_read": round(best * 1e3, 1),
+                     "gbs": round((gib << 30) / (best * 1e-3) / 1e9, 1)}
     out["frac_of_8tbs"] = {k: round(out[k]["gbs"] / 8000.0, 3) for k in ("ordinary", "nontemporal")}
     return out
 
@@ -526,6 +530,8 @@ def main():
     ap.add_argument("--read-ceiling", action="store_true",
                     help="only measure the HBM read rate of a plain 4 GiB read (moe_read_probe) "
                          "with ordinary and with non-temporal loads, and exit")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the HBM read-ceiling side measurement of the default run")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-FFN side measurements of the default run")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG",
@@ -625,6 +631,13 @@ def main():
             "stage_ms": {k: round(v, 4) for k, v in res["stage_ms"].items()},
         },
     }
+    if args.workload == "decode" and not args.no_read_ceiling:
+        # the practical HBM read ceiling, measured right after the decode
+        # steps, next to the decode roofline's nominal 8 TB/s
+        rc = read_ceiling(gib=4, reps=10)
+        rc["roofline_achieved_over_nontemporal"] = round(rf["achieved"] / rc["nontemporal"]["gbs"], 4)
+        line["read_ceiling"] = rc
+        torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res)
     if args.workload == "decode" and not args.no_prefill:
