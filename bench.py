@@ -207,6 +207,33 @@ def write_traffic(pmc_root, commands):
     print("\n".join(text))
 
 
+def summarize_lds(root, command):
+    """From rocprofv3 --pmc runs <root>/<workload>/run_counter_collection.csv
+    (workload = prefill, long) with the LDS and wait counters: the share of
+    cycles the LDS is active and the waves wait on LDS or on any counter."""
+    import collections
+    lines = ["", "# Second pass (rocprofv3 --pmc, its own run per workload): LDS activity and wait cycles",
+             f"#   {command}",
+             "#   LDS_active = SQ_LDS_IDX_ACTIVE / (256 CUs x cycles); LDS_wait and any_wait = "
+             "SQ_WAIT_INST_LDS and SQ_WAIT_ANY over SQ_WAVE_CYCLES",
+             f"{'workload':9s} {'kernel':8s} {'LDS_active':>10s} {'LDS_wait':>9s} {'any_wait':>9s}"]
+    for wl_name in ("prefill", "long"):
+        disp = collections.defaultdict(dict)
+        for r in _read_csv(os.path.join(root, wl_name, "run_counter_collection.csv")):
+            disp[(r["Kernel_Name"], r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
+        for tag, key in (("gate_up", "expert_gemm_lds_kernel<0>"), ("down", "expert_gemm_lds_kernel<1>")):
+            ds = [d for (k, _), d in disp.items() if key in k]
+            if not ds:
+                continue
+            m = {c: sum(d[c] for d in ds) / len(ds) for c in ds[0]}
+            cycles = m["GRBM_GUI_ACTIVE"] / 8
+            lines.append(f"{wl_name:9s} {tag:8s} {100 * m['SQ_LDS_IDX_ACTIVE'] / (256 * cycles):9.1f}% "
+                         f"{100 * m['SQ_WAIT_INST_LDS'] / m['SQ_WAVE_CYCLES']:8.1f}% "
+                         f"{100 * m['SQ_WAIT_ANY'] / m['SQ_WAVE_CYCLES']:8.1f}%")
+    print("\n".join(lines))
+    return lines
+
+
 def summarize_mfma(root, command):
     """From rocprofv3 --pmc runs <root>/<workload>/run_counter_collection.csv
     (workload = prefill, long) over the LDS-pipelined GEMMs, the per-dispatch
@@ -539,8 +566,9 @@ def main():
                          "a rocprofv3 kernel_stats.csv (and of its kernel trace per launch shape)")
     ap.add_argument("--write-traffic", nargs="+", metavar="ARG",
                     help="offline: PMC_ROOT COMMAND... -> profiles/traffic.json")
-    ap.add_argument("--summarize-mfma", nargs=3, metavar=("PMC_ROOT", "OUT", "COMMAND"),
-                    help="offline: MFMA/LDS counter runs (prefill, long) -> a short summary")
+    ap.add_argument("--summarize-mfma", nargs="+", metavar="ARG",
+                    help="offline: PMC_ROOT OUT COMMAND [LDS_PMC_ROOT LDS_COMMAND]: MFMA (and "
+                         "LDS/wait) counter runs over prefill and long -> a short summary")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(*args.summarize_stats)
@@ -549,9 +577,12 @@ def main():
         write_traffic(args.write_traffic[0], args.write_traffic[1:])
         return
     if args.summarize_mfma:
-        root, out, command = args.summarize_mfma
+        root, out, command = args.summarize_mfma[:3]
+        lines = summarize_mfma(root, command)
+        if len(args.summarize_mfma) == 5:
+            lines += summarize_lds(*args.summarize_mfma[3:])
         with open(out, "w") as f:
-            f.write("\n".join(summarize_mfma(root, command)) + "\n")
+            f.write("\n".join(lines) + "\n")
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: there is no multi-GPU path; --gpus must be 1.",
