@@ -35,7 +35,10 @@
 //    when their data has landed.)
 //  - Weights are used by one wave only and skip LDS: packed tiles go straight
 //    into a 3-slot register ring.  One 64-wide stage of a packed 16-row tile
-//    is 1024 contiguous elements.
+//    is 1024 contiguous elements.  When the row block is its group's only
+//    one, the workgroup is its weight tile's single reader and the loads are
+//    non-temporal (a higher HBM read rate); otherwise they are ordinary, so
+//    the sibling blocks find the tile in L2.
 //  - Stage s issues the weights and the tokens of stage s+2, multiplies its
 //    four k chunks
 //    (the LDS reads of chunk q+1 in flight under the MFMAs of chunk q), and
