@@ -119,6 +119,23 @@ def test_bias_forcing_selects_the_forced_set():
     assert (rg["counts"][forced.numpy()] == 64).all() and rg["counts"].sum() == 256
 
 
+def test_mixed_single_and_multi_block_groups():
+    """One launch with both weight-load kinds: a biased hot expert spans
+    several row blocks (ordinary loads, shared through L2) while the other
+    experts fit one block each (non-temporal loads); register-streaming
+    (16-row blocks) and LDS-pipelined (192-row blocks) kernels."""
+    for seed, T, H, E, K, I, Is, hot, bn in ((124, 48, 256, 24, 4, 64, 64, (5, 17), 16),
+                                              (125, 1200, 256, 8, 2, 128, 128, (3,), 192)):
+        g = _small(seed, T, H, E, K, I, Is)
+        b = g["b"].clone()
+        b[list(hot)] += 3.0
+        g["b"] = b
+        counts = _run(g, K)[1]["counts"]
+        cold = np.delete(counts, list(hot))
+        assert (counts[list(hot)] > bn).all() and ((cold > 0) & (cold <= bn)).any(), counts
+        _check_case(g, K)
+
+
 def test_all_ties_take_lowest_indices():
     g = _small(122, 16, 256, 20, 5, 64, 64, bias_std=0.0)
     g["Wr"] = torch.zeros_like(g["Wr"])
