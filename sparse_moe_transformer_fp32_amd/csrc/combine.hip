@@ -77,7 +77,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   *reinterpret_cast<u32x4*>(y + (size_t)t * H + c) = out;
 }
 
-// One workgroup per row, the row's H columns in chunks of 8 per thread.
+// One workgroup per row of min(1024, H/8) threads (rounded up to whole
+// waves): one chunk of 8 columns per thread up to H = 8192, two above.  (A
+// 256-thread workgroup with the row's chunks taken one after another per
+// thread left the loads of a thread's second chunk waiting on its first.)
 //   FUSED = false:  r = r_in (+ y_add)
 //   FUSED = true:   r = r_in + (sum_j o[slot_pos[t,j]] + o[KT + t]), the
 //                   combine of the layer folded into the residual add: the
@@ -85,8 +88,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 //                   last) and added to r_in before the one rounding to bf16.
 // r is stored to r_out as bf16; then x_out = bf16(r / sqrt(mean(r^2) + eps)
 // * (1 + gamma)) from the stored bf16 r, the sum of squares reduced in a
-// fixed order.  Each element of r_in/r_out is read and written by the same
-// thread, so r_out may alias r_in.
+// fixed order (within each wave by shuffles, then the wave partials in wave
+// order).  Each element of r_in/r_out is read and written by the same
+// thread, so r_out may alias r_in.  r_out and x_out are written with
+// non-temporal stores: every byte is written once and the rows stream out
+// (faster here; in the combine kernel above the same store was not).
 struct ResidualArgs {
   const uint16_t* r_in;
   const uint16_t* y_add;     // FUSED = false; may be null
@@ -100,16 +106,17 @@ struct ResidualArgs {
 };
 
 template <bool FUSED>
-__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
-  __shared__ float s_part[4];
+__global__ __launch_bounds__(1024) void residual_rmsnorm_kernel(ResidualArgs a) {
+  __shared__ float s_part[16];
+  const int nt = blockDim.x;
   const int t = blockIdx.x;
   const int H = a.H;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float ss = 0.f;
-  float v[8][8];  // H <= 16384: at most 8 chunks of 8 columns per thread
+  float v[2][8];  // H <= 16384, nt = min(1024, H / 8): at most 2 chunks per thread
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {
-    const int c = (ch * 256 + threadIdx.x) * 8;
+  for (int ch = 0; ch < 2; ++ch) {
+    const int c = (ch * nt + threadIdx.x) * 8;
     if (c < H) {
       const u32x4 rin = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.r_in + (size_t)t * H + c));
       float f[8];
@@ -119,15 +126,30 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) y[i] = 0.f;
       if (FUSED) {
-        // (one row at a time: this kernel keeps the whole row for the norm,
-        // and holding all K slot vectors as well halves its occupancy)
+        // slot rows 8 at a time (all of them for K = 8): their loads in
+        // flight together, then added in slot order.  Batches of 16 raise
+        // register use and lower occupancy, and were slower; batches of 4
+        // were no faster.
         add = true;
-        for (int j = 0; j < a.K; ++j) {
-          const int row = a.slot_pos[(size_t)t * a.K + j];
-          float fo[8];
-          bf16x8_to_f32(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.o + (size_t)row * H + c)), fo);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) y[i] += fo[i];
+        for (int j0 = 0; j0 < 16; j0 += 8) {
+          if (j0 < a.K) {
+            u32x4 ov[8];
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj)
+              if (j0 + jj < a.K)
+                ov[jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(
+                    a.o + (size_t)a.slot_pos[(size_t)t * a.K + j0 + jj] * H + c));
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) {
+              if (j0 + jj < a.K) {
+                float fo[8];
+                bf16x8_to_f32(ov[jj], fo);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] += fo[i];
+              }
+            }
+          }
         }
         if (a.has_shared) {
           float fo[8];
@@ -143,7 +165,7 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
         u32x4 pk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) pk[i] = pack2(f[2 * i] + y[2 * i], f[2 * i + 1] + y[2 * i + 1]);
-        if (a.r_out) *reinterpret_cast<u32x4*>(a.r_out + (size_t)t * H + c) = pk;
+        if (a.r_out) __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.r_out + (size_t)t * H + c));
         bf16x8_to_f32(pk, f);  // continue from the stored bf16 value
       }
 #pragma unroll
@@ -158,11 +180,12 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
   for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
   if (lane == 0) s_part[wave] = ss;
   __syncthreads();
-  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  float tot = 0.f;
+  for (int w = 0; w < nt / 64; ++w) tot += s_part[w];
   const float inv = 1.0f / sqrtf(tot / (float)H + a.eps);
 #pragma unroll
-  for (int ch = 0; ch < 8; ++ch) {
-    const int c = (ch * 256 + threadIdx.x) * 8;
+  for (int ch = 0; ch < 2; ++ch) {
+    const int c = (ch * nt + threadIdx.x) * 8;
     if (c < H) {
       u32x4 pk;
 #pragma unroll
@@ -174,7 +197,7 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(ResidualArgs a) {
         }
         pk[i] = pack2(v[ch][2 * i] * inv * g0, v[ch][2 * i + 1] * inv * g1);
       }
-      *reinterpret_cast<u32x4*>(a.x_out + (size_t)t * H + c) = pk;
+      __builtin_nontemporal_store(pk, reinterpret_cast<u32x4*>(a.x_out + (size_t)t * H + c));
     }
   }
 }
@@ -187,13 +210,19 @@ hipError_t launch_combine(const Plan& p, const uint16_t* o, const int32_t* slot_
   return hipGetLastError();
 }
 
+// one chunk of 8 columns per thread up to H = 8192, two above
+static int residual_threads(int H) {
+  const int n = (H / 8 + 63) / 64 * 64;
+  return n < 1024 ? n : 1024;
+}
+
 hipError_t launch_residual_rmsnorm(int T, int H, const uint16_t* r_in, const uint16_t* y_add,
                                    const float* gamma, float eps, uint16_t* r_out,
                                    uint16_t* x_out, hipStream_t s) {
   ResidualArgs a{};
   a.r_in = r_in; a.y_add = y_add; a.gamma = gamma; a.eps = eps;
   a.r_out = r_out; a.x_out = x_out; a.H = H;
-  hipLaunchKernelGGL(residual_rmsnorm_kernel<false>, dim3(T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(residual_rmsnorm_kernel<false>, dim3(T), dim3(residual_threads(H)), 0, s, a);
   return hipGetLastError();
 }
 
@@ -204,7 +233,7 @@ hipError_t launch_combine_residual(const Plan& p, const uint16_t* o, const int32
   a.r_in = r_in; a.o = o; a.slot_pos = slot_pos; a.gamma = gamma; a.eps = eps;
   a.r_out = r_out; a.x_out = x_out;
   a.H = p.H; a.K = p.K; a.KT = p.KT; a.has_shared = p.Is > 0 ? 1 : 0;
-  hipLaunchKernelGGL(residual_rmsnorm_kernel<true>, dim3(p.T), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(residual_rmsnorm_kernel<true>, dim3(p.T), dim3(residual_threads(p.H)), 0, s, a);
   return hipGetLastError();
 }
 
