@@ -238,9 +238,13 @@ def test_flash_skew_mild_sampled():
 
 
 # ---------------------------------------------------------------- RMSNorm glue
-def test_residual_rmsnorm_matches_oracle():
+@pytest.mark.parametrize("H", [1152, 9216, 16384])
+def test_residual_rmsnorm_matches_oracle(H):
+    """H = 1152: a partly filled last wave; above 8192 each thread takes a
+    second 8-column chunk (9216: only part of the workgroup)."""
+    print(f"residual_rmsnorm H={H}", flush=True)
     gen = torch.Generator().manual_seed(7)
-    T, H = 50, 1152
+    T = 50
     r = (torch.randn(T, H, generator=gen) * 3).to(torch.bfloat16).to(DEV)
     yv = torch.randn(T, H, generator=gen).to(torch.bfloat16).to(DEV)
     gamma = (torch.randn(H, generator=gen) * 0.1).to(DEV)
@@ -349,6 +353,7 @@ FUSED = {  # name: (seed, T, H, E, K, I, Is)
     "nb1": (140, 40, 384, 24, 4, 128, 64),
     "lds": (141, 600, 256, 8, 2, 128, 128),
     "no_shared": (142, 30, 256, 16, 4, 64, 0),
+    "wide_h": (143, 24, 9216, 8, 2, 64, 64),   # two column chunks per thread
 }
 
 
