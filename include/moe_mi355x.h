@@ -253,7 +253,8 @@ moe_status moe_pack_weights_strided(const uint16_t* src, uint16_t* dst, int32_t 
  *   x_out  = bf16( r' / sqrt(mean(r'^2) + eps) * (1 + gamma) )
  * where r' is the bf16 value stored for r.  gamma [H] fp32 may be NULL
  * (gain 1).  r_out may be NULL when y_add is NULL; x_out may be NULL (no
- * norm).  r_out may alias r_in.  H must be a multiple of 128; eps >= 0. */
+ * norm).  r_out may alias r_in.  H must be a multiple of 128 in [128,
+ * 16384] (MOE_ERR_SHAPE otherwise); eps >= 0. */
 moe_status moe_residual_rmsnorm(int32_t T, int32_t H, const uint16_t* r_in,
                                 const uint16_t* y_add, const float* gamma, float eps,
                                 uint16_t* r_out, uint16_t* x_out, hipStream_t stream);
