@@ -386,26 +386,30 @@ __device__ inline void score_key(float l, float b, float* sg, float* kk) {
 // One 64-thread workgroup (one wave) per token: add the S split-H partial
 // logits of each expert (contiguous, loaded as 16-byte vectors, all loads
 // issued before the adds; fixed order), then sigmoid, bias and wave_select.
-// C = ceil(E/64) expert slots per lane, fixed at compile time.
-template <int C>
+// C = ceil(E/64) expert slots per lane, fixed at compile time.  QN = 16-byte
+// vectors per expert: 8 holds up to 32 splits, four experts' splits in
+// flight at a time (a 128-VGPR buffer); 1 holds up to 4 splits, every
+// expert's in flight at once, in few enough registers for a higher
+// occupancy (many tokens, where the router splits H at most 4 ways).
+template <int C, int QN>
 __global__ __launch_bounds__(64) void route_topk_kernel(
     const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E,
     int K, float scale, int norm, int biw, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ keys_out, float* __restrict__ scores_out) {
+  constexpr int CB = QN == 1 ? C : 4;   // expert slots per load batch
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
   const float* prow = partial + (size_t)t * E * S;
 
   float key[C], sc[C];
-  // four experts' splits in flight at a time keeps the buffer at 128 VGPRs
 #pragma unroll
-  for (int c0 = 0; c0 < C; c0 += 4) {
-    f32x4 v[4][8];
+  for (int c0 = 0; c0 < C; c0 += CB) {
+    f32x4 v[CB][QN];
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < CB; ++cc) {
       const int e = min((c0 + cc) * 64 + lane, E - 1);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < QN; ++q) {
         if (c0 + cc < C && S >= 4 && q < S / 4)
           v[cc][q] = *reinterpret_cast<const f32x4*>(prow + (size_t)e * S + 4 * q);
         else if (c0 + cc < C && S < 4 && q == 0)
@@ -415,12 +419,12 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < CB; ++cc) {
       const int c = c0 + cc;
       if (c < C) {
         float l = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q)
+        for (int q = 0; q < QN; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j) l += v[cc][q][j];
         key[c] = -INFINITY;
@@ -734,9 +738,14 @@ hipError_t launch_route_topk(const Plan& p, const float* partial, const float* b
   const int C = (p.E + 63) / 64;
 #define SMOE_TOPK(CC)                                                                          \
   case CC:                                                                                     \
-    hipLaunchKernelGGL(route_topk_kernel<CC>, dim3(p.T), dim3(64), 0, s, partial,              \
-                       p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx, topk_w, \
-                       keys, scores);                                                          \
+    if (p.route_splits <= 4)                                                                   \
+      hipLaunchKernelGGL((route_topk_kernel<CC, 1>), dim3(p.T), dim3(64), 0, s, partial,       \
+                         p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx,      \
+                         topk_w, keys, scores);                                                \
+    else                                                                                       \
+      hipLaunchKernelGGL((route_topk_kernel<CC, 8>), dim3(p.T), dim3(64), 0, s, partial,       \
+                         p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx,      \
+                         topk_w, keys, scores);                                                \
     break;
   switch (C) {
     SMOE_TOPK(1) SMOE_TOPK(2) SMOE_TOPK(3) SMOE_TOPK(4) SMOE_TOPK(5) SMOE_TOPK(6)
