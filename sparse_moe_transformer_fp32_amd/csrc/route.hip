@@ -272,19 +272,29 @@ __global__ __launch_bounds__(256, 2) void route_logits_wide_kernel(
   if (st + 4 < nst) stage(std::integral_constant<int, 4>{}, st + 4);
 
   // accumulator register j of fragment (m, n): expert 16 m + 4 (lane / 16) + j,
-  // token 16 n + lane % 16; partial sums stored [T][E][S]
+  // token 16 n + lane % 16.  Partial sums are stored [T][S][E], so a lane's
+  // four registers of a fragment are four consecutive floats of one row:
+  // one 16-byte store (the row starts 16-byte aligned when E % 4 == 0, and e
+  // is a multiple of 4).  ([T][E][S] took one 4-byte store per register,
+  // 64 scattered writes per instruction.)
   const int S = gridDim.z;
+  const bool vec = (E & 3) == 0;
 #pragma unroll
   for (int n = 0; n < 4; ++n) {
     const int t = t0 + 16 * n + (lane & 15);
     if (t >= T) continue;
+    float* row = partial + ((size_t)t * S + split) * E;
 #pragma unroll
-    for (int m = 0; m < 3; ++m)
+    for (int m = 0; m < 3; ++m) {
+      const int e = e0 + 16 * m + 4 * (lane >> 4);
+      if (vec && e < E) {
+        *reinterpret_cast<f32x4*>(row + e) = acc[m][n];
+      } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int e = e0 + 16 * m + 4 * (lane >> 4) + j;
-        if (e < E) partial[((size_t)t * E + e) * S + split] = acc[m][n][j];
+        for (int j = 0; j < 4; ++j)
+          if (e + j < E) row[e + j] = acc[m][n][j];
       }
+    }
   }
 }
 
@@ -390,8 +400,12 @@ __device__ inline void score_key(float l, float b, float* sg, float* kk) {
 // vectors per expert: 8 holds up to 32 splits, four experts' splits in
 // flight at a time (a 128-VGPR buffer); 1 holds up to 4 splits, every
 // expert's in flight at once, in few enough registers for a higher
-// occupancy (many tokens, where the router splits H at most 4 ways).
-template <int C, int QN>
+// occupancy.  Both read the [T][E][S] partial sums of route_logits_kernel.
+// QN = 0 reads the [T][S][E] partial sums of route_logits_wide_kernel, SW
+// = S splits (1, 2, 4 or 8, fixed at compile time): one float per split and
+// expert, each load coalesced over the wave's 64 experts, all in flight at
+// once.
+template <int C, int QN, int SW>
 __global__ __launch_bounds__(64) void route_topk_kernel(
     const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E,
     int K, float scale, int norm, int biw, int32_t* __restrict__ topk_idx,
@@ -402,6 +416,30 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
   const float* prow = partial + (size_t)t * E * S;
 
   float key[C], sc[C];
+  if constexpr (QN == 0) {
+    const float* srow = partial + (size_t)t * SW * E;
+    float v[C][SW];
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int e = min(c * 64 + lane, E - 1);
+#pragma unroll
+      for (int s = 0; s < SW; ++s) v[c][s] = srow[(size_t)s * E + e];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      float l = 0.f;
+#pragma unroll
+      for (int s = 0; s < SW; ++s) l += v[c][s];
+      key[c] = -INFINITY;
+      sc[c] = 0.f;
+      const int e = c * 64 + lane;
+      if (e < E) {
+        score_key(l, bias[e], &sc[c], &key[c]);
+        if (keys_out) keys_out[(size_t)t * E + e] = sc[c] + bias[e];
+        if (scores_out) scores_out[(size_t)t * E + e] = sc[c];
+      }
+    }
+  } else {
 #pragma unroll
   for (int c0 = 0; c0 < C; c0 += CB) {
     f32x4 v[CB][QN];
@@ -437,6 +475,7 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
         }
       }
     }
+  }
   }
   wave_select<C>(key, sc, E, K, scale, norm, biw, topk_idx + (size_t)t * K,
                  topk_w + (size_t)t * K);
@@ -732,30 +771,51 @@ hipError_t launch_route_logits(const Plan& p, const uint16_t* x, const float* W,
   return hipGetLastError();
 }
 
+template <int C, int QN, int SW>
+static void topk_launch(const Plan& p, const float* partial, const float* bias, float scale,
+                        int norm, int biw, int32_t* topk_idx, float* topk_w, float* keys,
+                        float* scores, hipStream_t s) {
+  hipLaunchKernelGGL((route_topk_kernel<C, QN, SW>), dim3(p.T), dim3(64), 0, s, partial,
+                     p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx, topk_w,
+                     keys, scores);
+}
+
+// the instantiation that reads the router's layout: [T][S][E] after the wide
+// router (S = 1, 2, 4 or 8), [T][E][S] otherwise
+template <int C>
+static hipError_t topk_for_layout(const Plan& p, const float* partial, const float* bias,
+                                  float scale, int norm, int biw, int32_t* topk_idx,
+                                  float* topk_w, float* keys, float* scores, hipStream_t s) {
+  if (p.route_tok == kRouteT) {
+    switch (p.route_splits) {
+      case 1: topk_launch<C, 0, 1>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s); break;
+      case 2: topk_launch<C, 0, 2>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s); break;
+      case 4: topk_launch<C, 0, 4>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s); break;
+      case 8: topk_launch<C, 0, 8>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else if (p.route_splits <= 4) {
+    topk_launch<C, 1, 0>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s);
+  } else {
+    topk_launch<C, 8, 0>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_route_topk(const Plan& p, const float* partial, const float* bias,
                              float scale, int norm, int biw, int32_t* topk_idx, float* topk_w,
                              float* keys, float* scores, hipStream_t s) {
-  const int C = (p.E + 63) / 64;
-#define SMOE_TOPK(CC)                                                                          \
-  case CC:                                                                                     \
-    if (p.route_splits <= 4)                                                                   \
-      hipLaunchKernelGGL((route_topk_kernel<CC, 1>), dim3(p.T), dim3(64), 0, s, partial,       \
-                         p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx,      \
-                         topk_w, keys, scores);                                                \
-    else                                                                                       \
-      hipLaunchKernelGGL((route_topk_kernel<CC, 8>), dim3(p.T), dim3(64), 0, s, partial,       \
-                         p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx,      \
-                         topk_w, keys, scores);                                                \
-    break;
-  switch (C) {
+  switch ((p.E + 63) / 64) {
+#define SMOE_TOPK(CC) \
+  case CC:            \
+    return topk_for_layout<CC>(p, partial, bias, scale, norm, biw, topk_idx, topk_w, keys, scores, s);
     SMOE_TOPK(1) SMOE_TOPK(2) SMOE_TOPK(3) SMOE_TOPK(4) SMOE_TOPK(5) SMOE_TOPK(6)
     SMOE_TOPK(7) SMOE_TOPK(8) SMOE_TOPK(9) SMOE_TOPK(10) SMOE_TOPK(11) SMOE_TOPK(12)
     SMOE_TOPK(13) SMOE_TOPK(14) SMOE_TOPK(15) SMOE_TOPK(16)
+#undef SMOE_TOPK
     default:
       return hipErrorInvalidValue;
   }
-#undef SMOE_TOPK
-  return hipGetLastError();
 }
 
 hipError_t launch_dispatch(const Plan& p, const RouteLaunch& r, hipStream_t s) {
