@@ -413,9 +413,19 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
   constexpr int CB = QN == 1 ? C : 4;   // expert slots per load batch
   const int lane = threadIdx.x;
   const int t = blockIdx.x;
-  const float* prow = partial + (size_t)t * E * S;
 
   float key[C], sc[C];
+  // expert slot c from its summed logit l: score, key, optional exports
+  auto finish = [&](int c, float l) {
+    key[c] = -INFINITY;
+    sc[c] = 0.f;
+    const int e = c * 64 + lane;
+    if (e < E) {
+      score_key(l, bias[e], &sc[c], &key[c]);
+      if (keys_out) keys_out[(size_t)t * E + e] = sc[c] + bias[e];
+      if (scores_out) scores_out[(size_t)t * E + e] = sc[c];
+    }
+  };
   if constexpr (QN == 0) {
     const float* srow = partial + (size_t)t * SW * E;
     float v[C][SW];
@@ -430,52 +440,38 @@ __global__ __launch_bounds__(64) void route_topk_kernel(
       float l = 0.f;
 #pragma unroll
       for (int s = 0; s < SW; ++s) l += v[c][s];
-      key[c] = -INFINITY;
-      sc[c] = 0.f;
-      const int e = c * 64 + lane;
-      if (e < E) {
-        score_key(l, bias[e], &sc[c], &key[c]);
-        if (keys_out) keys_out[(size_t)t * E + e] = sc[c] + bias[e];
-        if (scores_out) scores_out[(size_t)t * E + e] = sc[c];
-      }
+      finish(c, l);
     }
   } else {
+    const float* prow = partial + (size_t)t * E * S;
 #pragma unroll
-  for (int c0 = 0; c0 < C; c0 += CB) {
-    f32x4 v[CB][QN];
+    for (int c0 = 0; c0 < C; c0 += CB) {
+      f32x4 v[CB][QN];
 #pragma unroll
-    for (int cc = 0; cc < CB; ++cc) {
-      const int e = min((c0 + cc) * 64 + lane, E - 1);
+      for (int cc = 0; cc < CB; ++cc) {
+        const int e = min((c0 + cc) * 64 + lane, E - 1);
 #pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        if (c0 + cc < C && S >= 4 && q < S / 4)
-          v[cc][q] = *reinterpret_cast<const f32x4*>(prow + (size_t)e * S + 4 * q);
-        else if (c0 + cc < C && S < 4 && q == 0)
-          v[cc][q] = f32x4{prow[(size_t)e * S], S > 1 ? prow[(size_t)e * S + 1] : 0.f, 0.f, 0.f};
-        else
-          v[cc][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < QN; ++q) {
+          if (c0 + cc < C && S >= 4 && q < S / 4)
+            v[cc][q] = *reinterpret_cast<const f32x4*>(prow + (size_t)e * S + 4 * q);
+          else if (c0 + cc < C && S < 4 && q == 0)
+            v[cc][q] = f32x4{prow[(size_t)e * S], S > 1 ? prow[(size_t)e * S + 1] : 0.f, 0.f, 0.f};
+          else
+            v[cc][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
-    }
 #pragma unroll
-    for (int cc = 0; cc < CB; ++cc) {
-      const int c = c0 + cc;
-      if (c < C) {
-        float l = 0.f;
+      for (int cc = 0; cc < CB; ++cc) {
+        if (c0 + cc < C) {
+          float l = 0.f;
 #pragma unroll
-        for (int q = 0; q < QN; ++q)
+          for (int q = 0; q < QN; ++q)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) l += v[cc][q][j];
-        key[c] = -INFINITY;
-        sc[c] = 0.f;
-        const int e = c * 64 + lane;
-        if (e < E) {
-          score_key(l, bias[e], &sc[c], &key[c]);
-          if (keys_out) keys_out[(size_t)t * E + e] = sc[c] + bias[e];
-          if (scores_out) scores_out[(size_t)t * E + e] = sc[c];
+            for (int j = 0; j < 4; ++j) l += v[cc][q][j];
+          finish(c0 + cc, l);
         }
       }
     }
-  }
   }
   wave_select<C>(key, sc, E, K, scale, norm, biw, topk_idx + (size_t)t * K,
                  topk_w + (size_t)t * K);
