@@ -451,8 +451,9 @@ def test_pack_column_slices_bit_exact():
 
 @pytest.mark.parametrize("name", ["dense_decode", "dense_prefill"])
 def test_dense_flash_shape(name):
-    """The model's dense FFN (H=4096, I=11264, 8 slices): every token at
-    T=16, sampled tokens at T=4096."""
+    """The model's dense FFN (H=4096, I=11264) with the benchmark's slice
+    counts (8 at T=16, 4 at T=4096): every token at T=16, sampled tokens at
+    T=4096."""
     from sparse_moe_transformer_fp32_amd.inputs import DENSE_WORKLOADS, make_dense_inputs
     wl = DENSE_WORKLOADS[name]
     x, wg, wu, wd = make_dense_inputs(wl, DEV)
