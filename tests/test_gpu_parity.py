@@ -90,6 +90,8 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "dispatch_blocks_ragged": (115, 1500, 256, 16, 4, 128, 64),
     "dispatch_blocks_E1024": (116, 1300, 256, 1024, 16, 64, 64),
     "wide_router_E100": (117, 1100, 2048, 100, 6, 128, 128),
+    # wide router, 8 H splits, E % 4 != 0: its partial sums go out as scalar stores
+    "wide_router_E30": (123, 1100, 1024, 30, 3, 64, 64),
     "max_H_lds": (119, 400, 16384, 8, 2, 128, 128),
     "max_I_lds": (120, 400, 256, 8, 2, 16384, 128),
     "max_I_Is_decode": (122, 12, 256, 8, 2, 16384, 16384),
