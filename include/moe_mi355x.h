@@ -36,7 +36,7 @@
  *     aligned.  Weights are read-only; x and y must not alias.
  *   - Calls are asynchronous on `stream` and never synchronise.  Argument
  *     checks run on the host before any HIP call, in the fixed order
- *     null -> shape -> option -> alignment -> workspace; a failed check
+ *     null -> layout -> shape -> option -> alignment -> workspace; a failed check
  *     returns a negative moe_status and sets moe_last_error().  A failed
  *     kernel launch returns MOE_ERR_DEVICE.  Faults during execution show
  *     up at the caller's next synchronisation of the stream.
@@ -54,16 +54,19 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = -1,        /* a required pointer is NULL                   */
   MOE_ERR_SHAPE = -2,       /* a size is out of the supported range         */
-  MOE_ERR_OPTION = -3,      /* an option value is invalid                   */
+  MOE_ERR_DTYPE = -3,       /* weights not in the layout the call reads
+                               (a weight struct whose `layout` is not
+                               MOE_LAYOUT_PACKED)                           */
   MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_workspace_bytes() */
   MOE_ERR_ALIGN = -5,       /* a device pointer is not 16-byte aligned      */
-  MOE_ERR_DEVICE = -6       /* a HIP call or kernel launch failed           */
+  MOE_ERR_DEVICE = -6,      /* a HIP call or kernel launch failed           */
+  MOE_ERR_OPTION = -7       /* an option value is invalid, or buffers alias */
 } moe_status;
 
 /* Layer sizes (host struct).
@@ -107,15 +110,34 @@ typedef struct { const float* W; const float* b; } moe_router;
  * 512 elements, tile (rt, kt) holding rows 16rt..16rt+15 and columns
  * 32kt..32kt+31 at element offset (rt*(C/32) + kt)*512; inside a tile,
  * W[16rt + r][32kt + c] sits at offset 8*(16*(c/8) + r) + c%8.  A packed
- * matrix has the same size as the row-major one. */
+ * matrix has the same size as the row-major one, so the pointer alone cannot
+ * tell the two apart: every weight struct therefore states its layout, and
+ * the compute calls refuse (MOE_ERR_DTYPE, before any HIP call) a struct that
+ * does not declare MOE_LAYOUT_PACKED.  A zero-initialised struct declares
+ * MOE_LAYOUT_ROW_MAJOR and is refused. */
+#define MOE_LAYOUT_ROW_MAJOR 0   /* the model's row-major matrices (not read by
+                                    the compute calls: pack them first)       */
+#define MOE_LAYOUT_PACKED 1      /* the output of moe_pack_weights            */
 
-/* Routed experts, bf16, PACKED: w_gate E x [I,H], w_up E x [I,H],
- * w_down E x [H,I] (matrix e at element offset e*I*H). */
-typedef struct { const uint16_t* w_gate; const uint16_t* w_up; const uint16_t* w_down; } moe_experts;
+/* Routed experts, bf16: layout (must be MOE_LAYOUT_PACKED), then
+ * w_gate E x [I,H], w_up E x [I,H], w_down E x [H,I] in that layout (matrix
+ * e at element offset e*I*H). */
+typedef struct {
+  int32_t layout;
+  const uint16_t* w_gate;
+  const uint16_t* w_up;
+  const uint16_t* w_down;
+} moe_experts;
 
-/* Shared expert, bf16, PACKED: w_gate [Is,H], w_up [Is,H], w_down [H,Is].
- * Pass NULL (or set dims.Is = 0) for a layer without a shared expert. */
-typedef struct { const uint16_t* w_gate; const uint16_t* w_up; const uint16_t* w_down; } moe_shared;
+/* Shared expert, bf16: layout (must be MOE_LAYOUT_PACKED), then w_gate
+ * [Is,H], w_up [Is,H], w_down [H,Is] in that layout.  Pass NULL (or set
+ * dims.Is = 0) for a layer without a shared expert. */
+typedef struct {
+  int32_t layout;
+  const uint16_t* w_gate;
+  const uint16_t* w_up;
+  const uint16_t* w_down;
+} moe_shared;
 
 /* Routing outputs (device buffers owned by the caller).
  *   topk_idx   [T,K] int32  selected experts, ascending per token
@@ -159,10 +181,10 @@ typedef struct {
   float eps;
 } moe_residual;
 
-/* A dense gated FFN (the model's first, dense layers), bf16, PACKED:
- * w_gate [I,H], w_up [I,H] as one packed matrix each; w_down as S packed
- * matrices [H, I/S], matrix s being columns s*I/S .. (s+1)*I/S - 1 of the
- * model's Wd [H,I] (see moe_dense_ffn). */
+/* A dense gated FFN (the model's first, dense layers), bf16, layout
+ * MOE_LAYOUT_PACKED: w_gate [I,H], w_up [I,H] as one packed matrix each;
+ * w_down as S packed matrices [H, I/S], matrix s being columns
+ * s*I/S .. (s+1)*I/S - 1 of the model's Wd [H,I] (see moe_dense_ffn). */
 typedef moe_shared moe_ffn;
 
 /* Byte offsets of the intermediates inside a workspace (host struct), for
@@ -199,6 +221,16 @@ moe_status moe_workspace_layout(const moe_dims* d, moe_ws_layout* out);
 
 /* Steps 1-4 of the layer: router logits, sigmoid, biased top-K, weights and
  * the expert-contiguous dispatch (counts, offsets, perm_token, slot_pos).
+ * Defining passages: LLM Atlas model card "Step-3.5-Flash", raw config field
+ * table (need_fp32_gate: the gate in fp32; moe_router_activation sigmoid;
+ * use_moe_router_bias; moe_top_k 8; norm_expert_weight;
+ * moe_router_scaling_factor 3; moe_num_experts 288), and the shd-paper.top
+ * summary, 方法详解 / 关键设计 (a gate gives one weight per expert and the
+ * highest-weighted experts are used).  The pages leave open where the bias
+ * enters; it is added after the sigmoid and steers the selection only
+ * (opts->bias_in_weights = 1 selects the other reading).  Equal keys go to
+ * the lower expert index; a token's slots are listed in ascending expert id
+ * and an expert's rows in ascending token order.
  *   d, opts  host structs; opts may be NULL (Flash defaults: scale 3,
  *            normalised, bias for selection only, no clamp)
  *   x        [T,H] bf16 token representations
@@ -213,9 +245,17 @@ moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
  * (bf16 MFMA, fp32 accumulation, h rounded to bf16), the shared expert on
  * every token, and the weighted combine back to token order (fp32 sum in
  * slot order, shared last, rounded once to bf16).
- *   experts      host struct of device pointers (all non-NULL)
+ * Defining passages: the routing as for moe_route; the hyper.ai summary,
+ * section 方法, and the paperlayer.ai summary, §2.2 (each token goes to 8 of
+ * 288 routed experts plus one always-on shared expert); the paperlayer.ai
+ * summary, App. B (SwiGLU experts: the gate activation times the up
+ * projection); the model card's raw config field table (hidden_size 4096,
+ * moe_intermediate_size 1280, share_expert_dim 1280, torch_dtype bfloat16).
+ * The shared expert is added with weight 1.
+ *   experts      host struct: layout MOE_LAYOUT_PACKED (else MOE_ERR_DTYPE)
+ *                and device pointers (all non-NULL)
  *   shared       host struct or NULL; must be non-NULL with non-NULL
- *                members iff d->Is > 0
+ *                members and layout MOE_LAYOUT_PACKED iff d->Is > 0
  *   y            [T,H] bf16 output
  *   routing_out  NULL, or a moe_routing as for moe_route to receive the
  *                routing (then the workspace keeps no copy of it)
@@ -227,7 +267,8 @@ moe_status moe_forward(const moe_dims* d, const moe_opts* opts, const uint16_t* 
                        hipStream_t stream);
 
 /* Convert n_mats row-major bf16 matrices [rows, cols] (consecutive in src)
- * into the packed layout above (consecutive in dst).  Done once when weights
+ * into the packed layout above (consecutive in dst); a weight struct that
+ * points at the result declares layout MOE_LAYOUT_PACKED.  Done once when weights
  * are loaded.  rows must be a multiple of 16, cols of 32; src and dst must
  * not overlap; both 16-byte aligned.  Asynchronous on `stream`. */
 moe_status moe_pack_weights(const uint16_t* src, uint16_t* dst, int32_t n_mats, int32_t rows,

@@ -15,12 +15,15 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libsmoe_gfx950.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
-MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_OPTION = 0, -1, -2, -3
-MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_DEVICE = -4, -5, -6
-STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_OPTION",
-                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_DEVICE"}
+MOE_OK, MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_DTYPE = 0, -1, -2, -3
+MOE_ERR_WORKSPACE, MOE_ERR_ALIGN, MOE_ERR_DEVICE, MOE_ERR_OPTION = -4, -5, -6, -7
+STATUS_NAMES = {0: "MOE_OK", -1: "MOE_ERR_NULL", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_DTYPE",
+                -4: "MOE_ERR_WORKSPACE", -5: "MOE_ERR_ALIGN", -6: "MOE_ERR_DEVICE",
+                -7: "MOE_ERR_OPTION"}
+# weight layouts a weight struct declares (only the packed one is read)
+MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_PACKED = 0, 1
 
 EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
             "moe_route", "moe_forward", "moe_forward_residual", "moe_residual_rmsnorm",
@@ -46,11 +49,21 @@ class Router(ctypes.Structure):
 
 
 class Experts(ctypes.Structure):
-    _fields_ = [("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
+    _fields_ = [("layout", ctypes.c_int32), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
 
 
 class Shared(ctypes.Structure):
-    _fields_ = [("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
+    _fields_ = [("layout", ctypes.c_int32), ("w_gate", _vp), ("w_up", _vp), ("w_down", _vp)]
+
+
+def packed_experts(w_gate, w_up, w_down) -> Experts:
+    """moe_experts for packed weights (the output of moe_pack_weights)."""
+    return Experts(MOE_LAYOUT_PACKED, _ptr(w_gate), _ptr(w_up), _ptr(w_down))
+
+
+def packed_shared(w_gate, w_up, w_down) -> Shared:
+    """moe_shared / moe_ffn for packed weights."""
+    return Shared(MOE_LAYOUT_PACKED, _ptr(w_gate), _ptr(w_up), _ptr(w_down))
 
 
 class Routing(ctypes.Structure):
@@ -285,17 +298,24 @@ class MoELayer:
                                            pack_weights(ws_down))
         self.tensors = (router_w, router_b, w_gate, w_up, w_down, ws_gate, ws_up, ws_down)
         self.router = Router(_ptr(router_w), _ptr(router_b))
-        self.experts = Experts(_ptr(w_gate), _ptr(w_up), _ptr(w_down))
-        self.shared = Shared(_ptr(ws_gate), _ptr(ws_up), _ptr(ws_down)) if self.Is else None
+        self.experts = packed_experts(w_gate, w_up, w_down)
+        self.shared = packed_shared(ws_gate, ws_up, ws_down) if self.Is else None
         self.opts = make_opts(**opts)
         self.device = router_w.device
         self._ws = None
+        self._retired = []
         if T_max:
             self.reserve(T_max)
 
     def reserve(self, T: int) -> int:
+        """Make the workspace hold a T-token call.  The size never falls as T
+        grows, so one reserve for the largest batch serves every smaller one.
+        A workspace that is outgrown is kept alive (HIP graphs captured on it
+        may still replay), never handed back to the allocator."""
         need = workspace_bytes(T, self.H, self.E, self.K, self.I, self.Is)
         if self._ws is None or self._ws.numel() < need:
+            if self._ws is not None:
+                self._retired.append(self._ws)
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return need
 
@@ -385,10 +405,11 @@ class DenseFFN:
         self.S = int(S)
         self.tensors = (pack_weights(w_gate), pack_weights(w_up),
                         pack_column_slices(w_down, self.S))
-        self.ffn = Shared(*[_ptr(t) for t in self.tensors])
+        self.ffn = packed_shared(*self.tensors)
         self.limit = float(swiglu_limit)
         self.device = w_gate.device
         self._ws = None
+        self._retired = []
         if T_max:
             self.reserve(T_max)
 
@@ -397,6 +418,8 @@ class DenseFFN:
         if need == 0:
             raise MoEError(MOE_ERR_SHAPE, last_error())
         if self._ws is None or self._ws.numel() < need:
+            if self._ws is not None:   # kept alive, as in MoELayer.reserve
+                self._retired.append(self._ws)
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
         return need
 

@@ -183,12 +183,8 @@ moe_status check_routing_align(const moe_routing* r) {
 
 namespace smoe {
 
-void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
-  *p = Plan{};
-  p->T = T; p->H = H; p->E = E; p->K = K; p->I = I; p->Is = Is;
-  p->KT = T * K;
-  p->rows_total = p->KT + (Is > 0 ? T : 0);
-
+// Router tiling: tokens per tile and the number of H splits for T tokens.
+static int route_tiling(int T, int H, int E, int* route_tok) {
   // router: 16-token tiles for decode, 64 otherwise; split H until the
   // launch has ~1024 workgroups (each split keeps >= 256 columns) so that
   // loads of many waves overlap
@@ -197,15 +193,44 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
     // many tokens: 256-token x 48-expert tiles (from 1024 tokens on they beat
     // the 64-token tiles on MI355X); split H while the launch stays within
     // two workgroups per CU
-    p->route_tok = 256;
+    *route_tok = 256;
     const int tiles = ((T + 255) / 256) * ((E + 47) / 48);
     while (S < 8 && tiles * 2 * S <= 512 && H % (2 * S * 64) == 0) S *= 2;
   } else {
-    p->route_tok = T <= 16 ? 16 : 64;
-    const int tiles = ((T + p->route_tok - 1) / p->route_tok) * ((E + 63) / 64);
+    *route_tok = T <= 16 ? 16 : 64;
+    const int tiles = ((T + *route_tok - 1) / *route_tok) * ((E + 63) / 64);
     const int min_cols = T <= 64 ? 128 : 256;
     while (S < 32 && tiles * S < 1024 && H % (2 * S * min_cols) == 0) S *= 2;
   }
+  return S;
+}
+
+// The largest S(t) * t over 1 <= t <= T.  The router's partial sums take
+// S * T * E floats; the split count falls as T grows, so S * T alone can
+// shrink from one T to the next.  Sizing the buffer by this maximum keeps
+// the workspace non-decreasing in T: one workspace sized for the largest
+// batch serves every smaller one.
+static size_t route_partial_rows(int T, int H, int E) {
+  size_t best = 0;
+  int rt;
+  for (int t = 1; t <= std::min(T, 1023); ++t)
+    best = std::max(best, (size_t)route_tiling(t, H, E, &rt) * t);
+  // from 1024 tokens on S depends on ceil(t / 256) only, so within each
+  // 256-token step the largest t is the step's last
+  for (int k = 4; 256 * (k - 1) < T; ++k) {
+    const int tt = std::min(256 * k, T);
+    best = std::max(best, (size_t)route_tiling(tt, H, E, &rt) * tt);
+  }
+  return best;
+}
+
+void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
+  *p = Plan{};
+  p->T = T; p->H = H; p->E = E; p->K = K; p->I = I; p->Is = Is;
+  p->KT = T * K;
+  p->rows_total = p->KT + (Is > 0 ? T : 0);
+
+  const int S = route_tiling(T, H, E, &p->route_tok);
   p->route_splits = S;
 
   // dispatch: one workgroup for small T, three kernels over 256-token blocks
@@ -245,7 +270,7 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
     return at;
   };
   const size_t KT = (size_t)p->KT;
-  p->ws_partial = take((size_t)S * T * E * 4);
+  p->ws_partial = take(route_partial_rows(T, H, E) * E * 4);
   p->ws_topk_idx = take(KT * 4);
   p->ws_topk_w = take(KT * 4);
   p->ws_counts = take((size_t)E * 4);
@@ -254,7 +279,11 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
   p->ws_slot = take(KT * 4);
   p->ws_row_token = take((size_t)p->rows_total * 4);
   p->ws_row_w = take((size_t)p->rows_total * 4);
-  p->ws_rb = take((size_t)p->rb_max * sizeof(RowBlock));
+  // the row-block list is sized for the finest cut (16-row blocks), a bound
+  // on rb_max for every batch up to T, so that the workspace never shrinks
+  // as T grows
+  const size_t rb_cap = (size_t)std::min(E, p->KT) + p->KT / 16 + (Is > 0 ? (T + 15) / 16 : 0);
+  p->ws_rb = take(std::max(rb_cap, (size_t)p->rb_max) * sizeof(RowBlock));
   p->ws_nrb = take(16);
   const size_t nblk = (size_t)p->dispatch_blocks;
   p->ws_lrank = take(nblk ? KT * 4 : 0);
@@ -327,8 +356,21 @@ moe_status moe_route(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
 
 namespace {
 
-// Checks shared by moe_forward and moe_forward_residual (null -> shape ->
-// option -> alignment; the workspace is checked by the caller).
+// The weight structs must declare the packed layout the GEMMs read: a
+// row-major matrix has the same size, so it would otherwise pass every other
+// check and give wrong output.
+moe_status check_layout(const char* fn, const char* what, int32_t layout) {
+  if (layout == MOE_LAYOUT_PACKED) return MOE_OK;
+  if (layout == MOE_LAYOUT_ROW_MAJOR)
+    return fail(MOE_ERR_DTYPE,
+                "%s: %s weights declare MOE_LAYOUT_ROW_MAJOR; pack them with moe_pack_weights "
+                "and declare MOE_LAYOUT_PACKED",
+                fn, what);
+  return fail(MOE_ERR_DTYPE, "%s: %s weights declare unknown layout %d", fn, what, layout);
+}
+
+// Checks shared by moe_forward and moe_forward_residual (null -> layout ->
+// shape -> option -> alignment; the workspace is checked by the caller).
 moe_status check_forward(const char* fn, const moe_dims* d, const moe_opts* opts,
                          const uint16_t* x, const moe_router* router,
                          const moe_experts* experts, const moe_shared* shared,
@@ -337,6 +379,8 @@ moe_status check_forward(const char* fn, const moe_dims* d, const moe_opts* opts
   if (d->Is > 0 && (!shared || !shared->w_gate || !shared->w_up || !shared->w_down))
     return fail(MOE_ERR_NULL, "%s: Is=%d but the shared expert weights are NULL", fn, d->Is);
   if (routing_out && (st = check_routing_out(routing_out, false, d->T == 0))) return st;
+  if ((st = check_layout(fn, "routed expert", experts->layout))) return st;
+  if (d->Is > 0 && (st = check_layout(fn, "shared expert", shared->layout))) return st;
   if ((st = check_shape(d))) return st;
   if ((st = check_opts(opts))) return st;
   if (misaligned(x) || misaligned(router->W) || misaligned(router->b) ||
@@ -494,6 +538,7 @@ moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint1
   if (!ffn || !ffn->w_gate || !ffn->w_up || !ffn->w_down || !ws || ((!x || !y) && T != 0))
     return fail(MOE_ERR_NULL, "moe_dense_ffn: NULL argument (x, ffn, ffn->w_*, y, ws)");
   moe_status st;
+  if ((st = check_layout("moe_dense_ffn", "dense FFN", ffn->layout))) return st;
   if ((st = check_dense(T, H, I, S))) return st;
   if (!isfinite(swiglu_limit) || swiglu_limit < 0.f)
     return fail(MOE_ERR_OPTION, "moe_dense_ffn: swiglu_limit must be finite and >= 0");

@@ -111,6 +111,18 @@ __device__ inline void wait_lds() {
   __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (3 << 14));
 }
 
+// Publishes this wave's LDS writes to the workgroup: wait until they are
+// done (lgkmcnt(0)), then meet the other waves at the barrier.  The barrier
+// builtin is not modelled as touching memory, so the empty asm statements
+// with a memory clobber on both sides keep the compiler from moving any
+// memory access across it.
+__device__ inline void lds_publish() {
+  asm volatile("" ::: "memory");
+  wait_lds();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // LDS bank swizzle of a token row's 16-byte chunks
 __device__ inline int row_swizzle(int R) { return (R >> 1) & 7; }
 
@@ -255,8 +267,7 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<kLoads>();
     write_t(ring[jt1], ts[jt1]);
-    wait_lds();
-    __builtin_amdgcn_s_barrier();
+    lds_publish();
     __builtin_amdgcn_sched_barrier(0);
     read_t(ring[jt1], 0, t[0]);
     __builtin_amdgcn_sched_barrier(0);
@@ -273,8 +284,7 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   __builtin_amdgcn_sched_barrier(0);
   wait_vmcnt<kLoads>();   // stage 0's tokens have arrived
   write_t(ring[0], ts[0]);
-  wait_lds();
-  __builtin_amdgcn_s_barrier();
+  lds_publish();
   __builtin_amdgcn_sched_barrier(0);
   read_t(ring[0], 0, t[0]);
   int s = 0;

@@ -73,13 +73,15 @@ def _vp(v):
 
 
 def _forward(dims=FLASH, opts=None, x=A, W=A, b=A, wg=A, wu=A, wd=A, shared=(A, A, A), y=2 * A,
-             ws=A, ws_bytes=None, routing=None):
+             ws=A, ws_bytes=None, routing=None, layout=None, shared_layout=None):
     lib = B.load()
     d = B.dims(*dims)
     o = opts if opts is not None else B.make_opts()
     r = B.Router(_vp(W), _vp(b))
-    e = B.Experts(_vp(wg), _vp(wu), _vp(wd))
-    sh = None if shared is None else B.Shared(*[_vp(v) for v in shared])
+    lay = B.MOE_LAYOUT_PACKED if layout is None else layout
+    e = B.Experts(lay, _vp(wg), _vp(wu), _vp(wd))
+    slay = B.MOE_LAYOUT_PACKED if shared_layout is None else shared_layout
+    sh = None if shared is None else B.Shared(slay, *[_vp(v) for v in shared])
     if ws_bytes is None:
         ws_bytes = B.workspace_bytes(*dims) if dims[0] >= 1 and dims[1] % 128 == 0 else 1 << 40
     return lib.moe_forward(ctypes.byref(d), ctypes.byref(o), _vp(x), ctypes.byref(r),
@@ -102,12 +104,57 @@ def test_forward_null_checks():
 
 
 def test_forward_check_order():
-    # null is reported before shape, shape before options, options before alignment
+    # null is reported before layout, layout before shape, shape before
+    # options, options before alignment
     bad_opts = B.make_opts(route_scale=-1.0)
     assert _forward(dims=(16, 4000) + FLASH[2:], x=0, ws_bytes=1) == B.MOE_ERR_NULL
+    assert _forward(dims=(16, 4000) + FLASH[2:], x=0, layout=0, ws_bytes=1) == B.MOE_ERR_NULL
+    assert _forward(dims=(16, 4000) + FLASH[2:], layout=0, ws_bytes=1) == B.MOE_ERR_DTYPE
     assert _forward(dims=(16, 4000) + FLASH[2:], opts=bad_opts, ws_bytes=1) == B.MOE_ERR_SHAPE
     assert _forward(opts=bad_opts, x=A + 2) == B.MOE_ERR_OPTION
     assert _forward(x=A + 2, ws_bytes=1) == B.MOE_ERR_ALIGN
+
+
+def test_row_major_weights_are_refused():
+    """A weight struct filled as the plain [E,I,H] / [E,H,I] row-major layout
+    (layout field left at 0, as a zero-initialised C struct has it) is refused
+    with MOE_ERR_DTYPE before any HIP call, instead of being read as packed
+    tiles; so is an unknown layout tag.  Only MOE_LAYOUT_PACKED passes."""
+    assert _forward(layout=B.MOE_LAYOUT_ROW_MAJOR) == B.MOE_ERR_DTYPE
+    assert "MOE_LAYOUT_ROW_MAJOR" in B.last_error() and "moe_pack_weights" in B.last_error()
+    assert _forward(shared_layout=B.MOE_LAYOUT_ROW_MAJOR) == B.MOE_ERR_DTYPE
+    assert "shared" in B.last_error()
+    assert _forward(layout=7) == B.MOE_ERR_DTYPE
+    assert "unknown layout 7" in B.last_error()
+    # no shared expert (Is = 0): the shared struct is not read at all
+    assert _forward(dims=FLASH[:5] + (0,), shared=None, ws_bytes=1) == B.MOE_ERR_WORKSPACE
+    R = B.Residual(_vp(3 * A), _vp(4 * A), _vp(5 * A), None, 1e-6)
+    lib = B.load()
+    d, o, r = B.dims(*FLASH), B.make_opts(), B.Router(_vp(A), _vp(A))
+    e = B.Experts(B.MOE_LAYOUT_ROW_MAJOR, _vp(A), _vp(A), _vp(A))
+    sh = B.Shared(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
+    assert lib.moe_forward_residual(ctypes.byref(d), ctypes.byref(o), _vp(A), ctypes.byref(r),
+                                    ctypes.byref(e), ctypes.byref(sh), ctypes.byref(R), None,
+                                    _vp(6 * A), 1 << 40, None) == B.MOE_ERR_DTYPE
+
+
+def test_workspace_never_shrinks_as_T_grows():
+    """One workspace sized for the largest batch serves every smaller one:
+    moe_workspace_bytes is non-decreasing in T (Flash shape over
+    T = 0..4096, and small shapes where the router's H split and the GEMM
+    row-block height change most often)."""
+    for shape in (FLASH[1:], (128, 1024, 1, 64, 0), (256, 16, 2, 64, 64), (1024, 30, 3, 64, 64)):
+        prev = 0
+        for T in range(0, 4097):
+            n = B.workspace_bytes(T, *shape)
+            assert n >= prev, (shape, T, n, prev)
+            prev = n
+    lib = B.load()
+    prev = 0
+    for T in range(0, 2049):
+        n = lib.moe_dense_workspace_bytes(T, 4096, 11264, 8)
+        assert n >= prev, (T, n, prev)
+        prev = n
 
 
 def test_forward_option_checks():
@@ -193,8 +240,8 @@ def _forward_res(res=None, x=A, ws_bytes=None, dims=FLASH):
     d = B.dims(*dims)
     o = B.make_opts()
     r = B.Router(_vp(A), _vp(A))
-    e = B.Experts(_vp(A), _vp(A), _vp(A))
-    sh = B.Shared(_vp(A), _vp(A), _vp(A))
+    e = B.Experts(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
+    sh = B.Shared(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
     if res is None:
         res = B.Residual(_vp(3 * A), _vp(4 * A), _vp(5 * A), None, 1e-6)
     if ws_bytes is None:
@@ -231,14 +278,16 @@ def test_dense_checks():
     assert lib.moe_dense_workspace_bytes(16, 4096, 11264 + 32, 8) == 0  # slices not % 64
     assert lib.moe_dense_workspace_bytes(-1, 4096, 11264, 8) == 0
     need = lib.moe_dense_workspace_bytes(16, 4096, 11264, 8)
-    f = B.Shared(_vp(A), _vp(A), _vp(A))
+    f = B.Shared(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
 
     def call(T=16, H=4096, I=11264, S=8, x=A, ffn=f, lim=0.0, y=2 * A, ws=3 * A, n=need):
         return lib.moe_dense_ffn(T, H, I, S, _vp(x), ctypes.byref(ffn) if ffn else None, lim,
                                  _vp(y), _vp(ws), n, None)
 
     assert call(x=0) == B.MOE_ERR_NULL
-    assert call(ffn=B.Shared(_vp(A), None, _vp(A))) == B.MOE_ERR_NULL
+    assert call(ffn=B.Shared(B.MOE_LAYOUT_PACKED, _vp(A), None, _vp(A))) == B.MOE_ERR_NULL
+    # row-major weights (layout left at 0) are refused, not read as packed
+    assert call(ffn=B.Shared(B.MOE_LAYOUT_ROW_MAJOR, _vp(A), _vp(A), _vp(A))) == B.MOE_ERR_DTYPE
     assert call(I=1000) == B.MOE_ERR_SHAPE
     assert call(H=4000) == B.MOE_ERR_SHAPE
     assert call(lim=-1.0) == B.MOE_ERR_OPTION
@@ -285,7 +334,7 @@ def test_empty_batch_host_paths():
     # call would zero on the device, so it is exercised on the GPU)
     bad = B.Routing(None, None, None, _vp(A), None, None, None, None)
     assert _forward(dims=empty, x=0, y=0, routing=bad) == B.MOE_ERR_NULL
-    ffn = B.Shared(_vp(A), _vp(A), _vp(A))
+    ffn = B.Shared(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
     need = lib.moe_dense_workspace_bytes(0, 4096, 11264, 8)
     assert lib.moe_dense_ffn(0, 4096, 11264, 8, None, ctypes.byref(ffn), 0.0, None, _vp(A), need,
                              None) == B.MOE_OK

@@ -6,7 +6,7 @@ LDS-pipelined kernels, and the fallback when shapes exclude them; the
 64-token and the 256-token router tiles), ragged tails, T=1, K=1, K=E, E not a multiple of 64, the
 largest E and K, no shared expert, the SwiGLU clamp and the alternative bias
 reading.  Flash-shaped cases run the same launch configuration as the
-benchmark: full outputs at T=16 and sampled rows at T=4096/8192.
+benchmark: full outputs at T=16 and T=4096, sampled rows at T=8192.
 """
 import numpy as np
 import pytest
@@ -146,18 +146,40 @@ def test_all_ties_take_lowest_indices():
     assert np.all(rg["topk_w"] == np.float32(3.0) * np.float32(0.5) / np.float32(2.5))
 
 
-def test_deterministic_and_permutation_equivariant():
-    g = _small(123, 96, 512, 24, 4, 128, 128)
-    y1, r1, _ = _run(g, 4)
-    y2, r2, _ = _run(g, 4)
-    assert np.array_equal(y1, y2)
+def _bitwise_twice_and_permuted(g, K, seed=0):
+    """Run the layer twice on the same inputs (outputs and routing must be
+    bitwise equal), then once on a seeded permutation of the tokens: y(P x)
+    must equal P y(x) bit for bit, and each token keep its experts."""
+    T = g["x"].shape[0]
+    y1, r1, _ = _run(g, K)
+    y2, r2, _ = _run(g, K)
+    assert np.array_equal(y1, y2), "two runs on the same inputs differ"
     for k in r1:
-        assert np.array_equal(r1[k], r2[k])
-    p = torch.randperm(96, generator=torch.Generator().manual_seed(0))
-    gp = dict(g, x=g["x"][p.to(DEV)].contiguous())
-    y3, r3, _ = _run(gp, 4)
-    assert np.array_equal(y3, y1[p.numpy()])
-    assert np.array_equal(r3["topk_idx"], r1["topk_idx"][p.numpy()])
+        assert np.array_equal(r1[k], r2[k]), f"routing {k} differs between two runs"
+    p = torch.randperm(T, generator=torch.Generator().manual_seed(seed))
+    gp = dict(g, x=g["x"][p.to(g["x"].device)].contiguous())
+    y3, r3, _ = _run(gp, K)
+    pn = p.numpy()
+    assert np.array_equal(y3, y1[pn]), "y(P x) != P y(x)"
+    assert np.array_equal(r3["topk_idx"], r1["topk_idx"][pn])
+    assert np.array_equal(r3["topk_w"], r1["topk_w"][pn])
+    assert np.array_equal(r3["counts"], r1["counts"])
+    return r1
+
+
+@pytest.mark.parametrize("case", [
+    # 16 rows per expert: the register-streaming kernels
+    (123, 96, 512, 24, 4, 128, 128),
+    # 300 rows per expert on average: the LDS-pipelined kernels (192-row
+    # blocks of 32-row fragments), experts over several row blocks, ragged
+    # last fragments
+    (126, 1200, 256, 8, 2, 128, 128),
+])
+def test_deterministic_and_permutation_equivariant(case):
+    print(f"case bitwise {case}", flush=True)
+    r = _bitwise_twice_and_permuted(_small(*case), case[4])
+    if case[1] == 1200:
+        assert (r["counts"] > 192).any(), r["counts"]   # experts over >= 2 row blocks
 
 
 def test_max_tokens_sampled():
@@ -217,8 +239,20 @@ def test_flash_decode_full():
     assert rg["counts"].sum() == 16 * 8
 
 
-def test_flash_prefill_sampled():
-    _flash_check("prefill", n_sample=512)
+def test_flash_prefill_full():
+    """T = 4096 at the Flash shape (the LDS-pipelined kernels, every expert
+    touched, ~114 rows each): routing on every token and the output on all
+    4096 rows against the float64 oracle."""
+    _flash_check("prefill")
+
+
+def test_flash_prefill_bitwise_deterministic_and_permutation_equivariant():
+    """The full-size prefill in the benchmark's launch configuration, run
+    twice (bitwise equal) and once on permuted tokens (y(P x) = P y(x) bit
+    for bit)."""
+    g, inp = _flash("prefill")
+    print("flash case prefill: run twice + permuted", flush=True)
+    _bitwise_twice_and_permuted(g, inp.wl.K, seed=3)
 
 
 def test_flash_skew_sampled():
