@@ -379,6 +379,30 @@ moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events);
 moe_status moe_read_probe(const void* buf, size_t bytes, int32_t nontemporal, void* sink,
                           hipStream_t stream);
 
+/* For callers that cannot allocate: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc.  moe_forward with the
+ * same arguments minus the workspace: the scratch memory comes from a fixed
+ * device array of MOE_NOALLOC_SCRATCH_BYTES inside the library (one per GPU,
+ * held until the process ends), so the call allocates nothing.
+ *   - The stream must belong to the current device (MOE_ERR_DEVICE
+ *     otherwise); the first call on a device looks up that device's array.
+ *   - Layers whose moe_workspace_bytes(d) exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     are refused with MOE_ERR_WORKSPACE (at the Flash shape: T > 290);
+ *     use moe_forward with a workspace for them.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (two streams, two threads) race and must not be made.
+ *     Nothing in it needs clearing between calls: no call depends on what
+ *     an earlier one left there (every scratch value a call uses, the same
+ *     call wrote first).  A routing output, if asked for, goes to the
+ *     caller's buffers as for moe_forward; the h and o intermediates stay in
+ *     the array (moe_ws_layout gives their offsets in it).
+ * Checks and errors are as for moe_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_noalloc(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                               const moe_router* router, const moe_experts* experts,
+                               const moe_shared* shared, uint16_t* y,
+                               const moe_routing* routing_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,7 +28,10 @@ MOE_LAYOUT_ROW_MAJOR, MOE_LAYOUT_PACKED = 0, 1
 EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_workspace_layout",
             "moe_route", "moe_forward", "moe_forward_residual", "moe_residual_rmsnorm",
             "moe_set_stage_events", "moe_pack_weights", "moe_pack_weights_strided",
-            "moe_dense_workspace_bytes", "moe_dense_ffn", "moe_expert_stats", "moe_read_probe"]
+            "moe_dense_workspace_bytes", "moe_dense_ffn", "moe_expert_stats", "moe_read_probe",
+            "moe_forward_noalloc"]
+# bytes of the library's fixed scratch array (moe_forward_noalloc)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 STAGES = ["route_logits", "route_topk", "dispatch", "gate_up", "down", "combine"]
 
 _vp = ctypes.c_void_p
@@ -112,6 +115,9 @@ def load() -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_forward.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Experts), P(Shared), _vp,
                                 P(Routing), _vp, ctypes.c_size_t, _vp]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Experts), P(Shared),
+                                        _vp, P(Routing), _vp]
     lib.moe_forward_residual.restype = ctypes.c_int
     lib.moe_forward_residual.argtypes = [P(Dims), P(Opts), _vp, P(Router), P(Experts), P(Shared),
                                          P(Residual), P(Routing), _vp, ctypes.c_size_t, _vp]
@@ -343,6 +349,24 @@ class MoELayer:
         return y
 
     __call__ = forward
+
+    def forward_noalloc(self, x: torch.Tensor, y: torch.Tensor,
+                        routing: Optional[Dict[str, torch.Tensor]] = None) -> torch.Tensor:
+        """moe_forward_noalloc: the layer with the library's fixed scratch
+        array instead of a workspace; y (and routing) are the caller's."""
+        lib = load()
+        _dev(x, "x", torch.bfloat16)
+        _dev(y, "y", torch.bfloat16)
+        T = x.shape[0]
+        d = dims(T, self.H, self.E, self.K, self.I, self.Is)
+        rs = _routing_struct(routing) if routing is not None else None
+        _check(lib.moe_forward_noalloc(ctypes.byref(d), ctypes.byref(self.opts), _ptr(x),
+                                       ctypes.byref(self.router), ctypes.byref(self.experts),
+                                       ctypes.byref(self.shared) if self.shared is not None
+                                       else None, _ptr(y),
+                                       ctypes.byref(rs) if rs is not None else None,
+                                       _stream(x.device)))
+        return y
 
     def forward_residual(self, x: torch.Tensor, r_in: torch.Tensor,
                          r_out: Optional[torch.Tensor] = None,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "moe_mi355x.h"
@@ -523,6 +524,85 @@ moe_status moe_forward_residual(const moe_dims* d, const moe_opts* opts, const u
     return fail(MOE_ERR_OPTION, "moe_forward_residual: x must not alias r_in or r_out");
   return forward_impl("moe_forward_residual", d, opts, x, router, experts, shared, nullptr, res,
                       routing_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// moe_forward_noalloc: the scratch memory is this fixed device array.  In
+// host code its name is a host-side stand-in, not a device address: host
+// code only ever uses the address hipGetSymbolAddress returns for the current
+// device, kept per device below.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current).
+moe_status device_scratch(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_DEVICE, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_DEVICE, "device %d out of the supported range [0, %d)", dev, kMaxDevices);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess)
+      return fail(MOE_ERR_DEVICE, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(MOE_ERR_DEVICE,
+                  "moe_forward_noalloc: the stream belongs to device %d but device %d is current",
+                  (int)sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(MOE_ERR_DEVICE, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(const moe_dims* d, const moe_opts* opts, const uint16_t* x,
+                               const moe_router* router, const moe_experts* experts,
+                               const moe_shared* shared, uint16_t* y,
+                               const moe_routing* routing_out, hipStream_t stream) {
+  if (!d || !router || !router->W || !router->b || !experts || !experts->w_gate ||
+      !experts->w_up || !experts->w_down || ((!x || !y) && d->T != 0))
+    return fail(MOE_ERR_NULL,
+                "moe_forward_noalloc: NULL argument (dims, x, router, router->W/b, "
+                "experts->w_*, y)");
+  moe_status st;
+  if ((st = check_forward("moe_forward_noalloc", d, opts, x, router, experts, shared,
+                          routing_out)))
+    return st;
+  if (misaligned(y)) return fail(MOE_ERR_ALIGN, "moe_forward_noalloc: y must be 16-byte aligned");
+  if (x == y && d->T != 0)
+    return fail(MOE_ERR_OPTION, "moe_forward_noalloc: x and y must not alias");
+  smoe::Plan p;
+  smoe::make_plan(d->T, d->H, d->E, d->K, d->I, d->Is, &p);
+  if (p.ws_total > MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_noalloc: this layer needs %zu bytes of scratch, more than the "
+                "fixed %u; call moe_forward with a workspace",
+                p.ws_total, (unsigned)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if ((st = device_scratch(stream, &ws))) return st;
+  return forward_impl("moe_forward_noalloc", d, opts, x, router, experts, shared, y, nullptr,
+                      routing_out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t moe_dense_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t S) {

@@ -354,3 +354,33 @@ def test_read_probe_checks():
     assert lib.moe_read_probe(_vp(A), 16384 + 16, 0, _vp(A), None) == B.MOE_ERR_SHAPE
     assert "multiple of 16384" in B.last_error()
     assert lib.moe_read_probe(_vp(A), 16384, 2, _vp(A), None) == B.MOE_ERR_OPTION
+
+
+def test_noalloc_host_checks():
+    """moe_forward_noalloc checks its arguments as moe_forward does, and
+    refuses a layer whose scratch need exceeds the fixed array, all on the
+    host before any HIP call."""
+    lib = B.load()
+    r = B.Router(_vp(A), _vp(A))
+    e = B.Experts(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
+    sh = B.Shared(B.MOE_LAYOUT_PACKED, _vp(A), _vp(A), _vp(A))
+    o = B.make_opts()
+
+    def call(dims=FLASH, x=A, y=2 * A, experts=e, opts=o):
+        d = B.dims(*dims)
+        return lib.moe_forward_noalloc(ctypes.byref(d), ctypes.byref(opts), _vp(x),
+                                       ctypes.byref(r), ctypes.byref(experts), ctypes.byref(sh),
+                                       _vp(y), None, None)
+
+    assert call(x=0) == B.MOE_ERR_NULL
+    assert call(experts=B.Experts(B.MOE_LAYOUT_ROW_MAJOR, _vp(A), _vp(A), _vp(A))) == B.MOE_ERR_DTYPE
+    assert call(dims=(16, 4000) + FLASH[2:]) == B.MOE_ERR_SHAPE
+    assert call(opts=B.make_opts(route_scale=-1.0)) == B.MOE_ERR_OPTION
+    assert call(y=2 * A + 2) == B.MOE_ERR_ALIGN
+    assert call(x=A, y=A) == B.MOE_ERR_OPTION
+    T_max = 1
+    while B.workspace_bytes(T_max + 1, *FLASH[1:]) <= B.NOALLOC_SCRATCH_BYTES:
+        T_max += 1
+    assert T_max == 290          # the Flash shape fits up to 290 tokens
+    assert call(dims=(T_max + 1,) + FLASH[1:]) == B.MOE_ERR_WORKSPACE
+    assert "moe_forward with a workspace" in B.last_error()
