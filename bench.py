@@ -164,14 +164,19 @@ def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
 # the gate/up kernel each counter workload launches (decode: register-streaming;
 # prefill: LDS-pipelined)
 GATE_UP_KERNEL = {"decode": "void smoe::expert_gemm_kernel<0,",
-                  "prefill": "void smoe::expert_gemm_lds_kernel<0>"}
+                  "prefill": "void smoe::expert_gemm_lds_kernel<0>",
+                  "long": "void smoe::expert_gemm_lds_kernel<0>",
+                  "skew": "void smoe::expert_gemm_lds_kernel<0>"}
 
 
 def write_traffic(pmc_root, commands):
     """From rocprofv3 --pmc runs laid out as <pmc_root>/<name>_<COUNTER>/
-    run_counter_collection.csv for name in copy/decode/prefill, compute the
-    per-dispatch HBM bytes of the gate/up kernel, scaled by what the same
-    counters read for a plain 1 GiB device copy, and record them."""
+    run_counter_collection.csv (name = copy, and any of decode / prefill /
+    long / skew present), compute the per-dispatch HBM bytes of every smoe
+    kernel, scaled by what the same counters read for a plain 1 GiB device
+    copy; write one summary per workload (profiles/hbm_bytes_<workload>.txt)
+    and record the gate/up kernel's bytes in profiles/traffic.json (entries
+    of workloads not in this run are kept)."""
     import collections
     def per_kernel(name, counter):
         agg = collections.defaultdict(list)
@@ -182,13 +187,17 @@ def write_traffic(pmc_root, commands):
     cf = max(v for k, v in per_kernel("copy", "FETCH_SIZE").items() if "copy" in k.lower())
     cw = max(v for k, v in per_kernel("copy", "WRITE_SIZE").items() if "copy" in k.lower())
     f_fetch, f_write = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    out = {}
-    text = [f"# HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by",
+    tpath = os.path.join(ROOT, "profiles", "traffic.json")
+    out = json.load(open(tpath)) if os.path.exists(tpath) else {}
+    head = [f"# HBM bytes per dispatch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB), scaled by",
             f"# a plain 1 GiB device copy: FETCH_SIZE read {cf:.0f} KiB -> factor {f_fetch:.4f};",
             f"# WRITE_SIZE read {cw:.0f} KiB -> factor {f_write:.4f}.", "# commands:"]
-    text += [f"#   {c}" for c in commands]
-    for wl in ("decode", "prefill"):
+    head += [f"#   {c}" for c in commands]
+    for wl in ("decode", "prefill", "long", "skew"):
+        if not os.path.isdir(os.path.join(pmc_root, f"{wl}_FETCH_SIZE")):
+            continue
         fe, wr = per_kernel(wl, "FETCH_SIZE"), per_kernel(wl, "WRITE_SIZE")
+        text = list(head)
         for k in sorted(fe):
             if "smoe" not in k:
                 continue
@@ -200,11 +209,11 @@ def write_traffic(pmc_root, commands):
                                         "fetch_kib": fe[k], "write_kib": wr.get(k, 0.0),
                                         "fetch_factor": f_fetch, "write_factor": f_write,
                                         "source_sha": _src_sha(KERNEL_SOURCES[wl])}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        with open(os.path.join(ROOT, "profiles", f"hbm_bytes_gate_up_down_{wl}.txt"), "w") as f:
+            f.write("\n".join(text) + "\n")
+        print("\n".join(text))
+    with open(tpath, "w") as f:
         json.dump(out, f, indent=1)
-    with open(os.path.join(ROOT, "profiles", "hbm_bytes_gate_up_down_decode_prefill.txt"), "w") as f:
-        f.write("\n".join(text) + "\n")
-    print("\n".join(text))
 
 
 def summarize_lds(root, command):
@@ -481,7 +490,8 @@ def cpu_baseline(res, max_tokens=16, budget_s=10.0):
             cpu_model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
     except (OSError, StopIteration):  # pragma: no cover
         pass
-    # repeat the call until about budget_s of CPU work (at most 10 calls)
+    # repeat the call until about budget_s of CPU work (at most 10 calls;
+    # a call longer than the budget is timed once)
     reps = 0
     t0 = time.perf_counter()
     while True:
@@ -533,6 +543,63 @@ def library_reference(reps=10):
     return out
 
 
+def side_layer_obj(wl_name, steps, warmup, cpu=False):
+    """One side workload of the default run (prefill, long, skew): whole-step
+    throughput, per-layer MFMA and HBM figures, both grouped GEMMs against
+    their MFMA roofline (HIP events on the launch stream; for the chained
+    long workload, the last layer's kernels), the attainable fraction
+    min(peak, intensity x 8 TB/s) / achieved, and for skewed routing the
+    per-expert load (count max/mean, share on the boosted experts)."""
+    import numpy as np
+    import torch
+    from sparse_moe_transformer_fp32_amd.inputs import boosted_experts
+    r = run_layer_bench(wl_name, steps, warmup)
+    wl, nl = r["wl"], r["n_layers"]
+    w = layer_work(wl, r["counts"])
+    ms = r["wall_ms"]
+    lay_ms = ms / nl
+    st = r["stage_ms"]
+    gu_ms, dn_ms = st["gate_up"], st["down"]
+    dn_flops = w["layer_flops"] - w["gu_flops"]
+    # the layer's floor: its FLOPs at the MFMA peak or its bytes at 8 TB/s
+    floor_ms = max(w["layer_flops"] / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                   w["layer_bytes"] / (HBM_PEAK_GBS * 1e9)) * 1e3
+    tkey = f"gate_up:{wl.name}"
+    out = {
+        "workload": f"{wl.name}: T={wl.T} tokens, Flash shape, {nl} layer(s)"
+                    + (f", router bias +{wl.bias_boost} on {wl.n_boost} seeded experts"
+                       if wl.n_boost else ", near-uniform routing"),
+        "tokens_per_s": round(wl.T / (ms / 1e3), 1),
+        "ms_per_step": round(ms, 4),
+        "ms_per_layer": round(lay_ms, 4),
+        "bf16_tflops": round(w["layer_flops"] / (lay_ms * 1e-3) / 1e12, 2),
+        "mfma_frac": round(w["layer_flops"] / (lay_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "hbm_gbs": round(w["layer_bytes"] / (lay_ms * 1e-3) / 1e9, 1),
+        "hbm_frac": round(w["layer_bytes"] / (lay_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "attainable_ms": round(floor_ms, 4),
+        "attainable_frac": round(floor_ms / lay_ms, 4),
+        "active_experts": w["n_active"],
+        "roofline_gate_up": roofline_obj("mfma", w["gu_flops"] / (gu_ms * 1e-3) / 1e12,
+                                         MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", _traffic(tkey)),
+        "roofline_down": roofline_obj("mfma", dn_flops / (dn_ms * 1e-3) / 1e12,
+                                      MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None),
+        "gate_up_hbm_gbs": round(w["gu_bytes"] / (gu_ms * 1e-3) / 1e9, 1),
+        "stage_ms": {k: round(v, 4) for k, v in st.items()},
+    }
+    c = r["counts"].astype(np.int64)
+    if wl.n_boost:
+        boost = boosted_experts(wl)
+        out["expert_load"] = {"count_max": int(c.max()), "count_mean": round(float(c.mean()), 2),
+                              "max_over_mean": round(float(c.max() / c.mean()), 3),
+                              "boosted": int(wl.n_boost),
+                              "share_on_boosted": round(float(c[boost].sum() / c.sum()), 4)}
+    if cpu:
+        out["cpu_baseline"] = cpu_baseline(r, max_tokens=wl.T, budget_s=15.0)
+    del r
+    torch.cuda.empty_cache()
+    return out
+
+
 def roofline_obj(bound, achieved, peak, unit, traffic):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -561,6 +628,10 @@ def main():
                     help="skip the HBM read-ceiling side measurement of the default run")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the dense-FFN side measurements of the default run")
+    ap.add_argument("--no-long", action="store_true",
+                    help="skip the long (T=32768 x 4 layers) side measurement of the default run")
+    ap.add_argument("--no-skew", action="store_true",
+                    help="skip the skewed-routing (T=8192) side measurement of the default run")
     ap.add_argument("--summarize-stats", nargs="+", metavar="ARG",
                     help="offline: STATS_CSV OUT COMMAND [TRACE_CSV] -> a short summary of "
                          "a rocprofv3 kernel_stats.csv (and of its kernel trace per launch shape)")
@@ -671,33 +742,27 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res)
-    if args.workload == "decode" and not args.no_prefill:
+    if args.workload == "decode":
         del res
         torch.cuda.empty_cache()
-        pre = run_layer_bench("prefill", max(5, args.steps // 5), 3)
-        pw = layer_work(pre["wl"], pre["counts"])
-        pms = pre["wall_ms"]
-        pgu = pre["stage_ms"]["gate_up"]
-        line["prefill"] = {
-            "workload": "prefill: T=4096 tokens, Flash shape, near-uniform routing",
-            "tokens_per_s": round(4096 / (pms / 1e3), 1),
-            "ms_per_step": round(pms, 4),
-            "bf16_tflops": round(pw["layer_flops"] / (pms * 1e-3) / 1e12, 2),
-            "mfma_frac": round(pw["layer_flops"] / (pms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "hbm_gbs": round(pw["layer_bytes"] / (pms * 1e-3) / 1e9, 1),
-            "hbm_frac": round(pw["layer_bytes"] / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "roofline_gate_up": roofline_obj("mfma", pw["gu_flops"] / (pgu * 1e-3) / 1e12,
-                                             MFMA_BF16_PEAK_TFLOPS, "TFLOP/s",
-                                             _traffic("gate_up:prefill")),
-            "gate_up_hbm_gbs": round(pw["gu_bytes"] / (pgu * 1e-3) / 1e9, 1),
-            "stage_ms": {k: round(v, 4) for k, v in pre["stage_ms"].items()},
-        }
-        del pre
-        torch.cuda.empty_cache()
-    if args.workload == "decode" and not args.no_dense:
-        line["dense"] = {n: run_dense_bench(n, max(5, args.steps // 5), 3)
-                         for n in ("dense_decode", "dense_prefill")}
-        torch.cuda.empty_cache()
+        side_steps = max(5, args.steps // 5)
+        if not args.no_prefill:
+            # the metric's MFMA figure is quoted at T=4096; the oracle is
+            # timed on the whole batch in the same run
+            line["prefill"] = side_layer_obj("prefill", side_steps, 3,
+                                             cpu=not args.no_cpu_baseline)
+            torch.cuda.empty_cache()
+        if not args.no_dense:
+            line["dense"] = {n: run_dense_bench(n, side_steps, 3)
+                             for n in ("dense_decode", "dense_prefill")}
+            torch.cuda.empty_cache()
+        if not args.no_long:
+            # the compute-bound regime: 4 chained layers at T=32768
+            line["long"] = side_layer_obj("long", 3, 1)
+            torch.cuda.empty_cache()
+        if not args.no_skew:
+            line["skew"] = side_layer_obj("skew", side_steps, 3)
+            torch.cuda.empty_cache()
     print(json.dumps(line), flush=True)
 
 
