@@ -39,12 +39,16 @@
 //    one, the workgroup is its weight tile's single reader and the loads are
 //    non-temporal (a higher HBM read rate); otherwise they are ordinary, so
 //    the sibling blocks find the tile in L2.
-//  - Stage s issues the weights and the tokens of stage s+2, multiplies its
-//    four k chunks
-//    (the LDS reads of chunk q+1 in flight under the MFMAs of chunk q), and
-//    before its last chunk stores stage s+1's tokens to LDS and meets the
-//    other waves at a barrier, so the first chunk of stage s+1 is read under
-//    that last chunk's MFMAs.
+//  - Stage s first writes stage s+1's tokens (loaded in stage s-1) to LDS,
+//    then multiplies its four k chunks.  The MFMAs of each chunk carry the
+//    instructions the pipeline needs next, one after each MFMA: the LDS
+//    reads of the next chunk's B operands, and this stage's global loads
+//    for stage s+2 (tokens during chunk 0, two weight loads during chunks 1
+//    and 2).  Issued in bursts instead, the loads and reads stalled both
+//    waves of a SIMD at the same point of every stage and left the matrix
+//    core idle.  Before the last chunk the waves meet at a barrier that
+//    publishes stage s+1's tokens, so the first chunk of stage s+1 is read
+//    under the last chunk's MFMAs.
 //  - The number of 32-token fragments with real rows (NA) is a template
 //    argument, so the MFMA stream has no branches, and the waves gather only
 //    those fragments' rows (ceil(NA/2) loads per wave per stage).
@@ -52,12 +56,13 @@
 //    the output tile in LDS, in the token ring's memory, and writes whole
 //    rows with 16-byte non-temporal stores.
 //
-// XCD-aware order: block b runs on XCD b % 8.  Work items, ordered (group,
-// weight tile, row block), are dealt to the XCDs in chunks of 32 in turn.
-// Workgroups that run side by side on one XCD then share weight tiles
-// (across an expert's row blocks, which the dispatch cuts to nearly equal
-// heights so that they keep pace) and token rows (across weight tiles)
-// through that XCD's L2, and no XCD is left with all of a heavy group.
+// XCD-aware order: block b runs on XCD b % 8.  The routed experts' row
+// blocks and the shared expert's are each cut into 8 contiguous ranges, one
+// per XCD, whose work items run group by group, weight tile by weight tile,
+// row block by row block: the workgroups that run side by side on one XCD
+// share weight tiles (across an expert's row blocks, which the dispatch cuts
+// to nearly equal heights so that they keep pace) and token rows (across
+// weight tiles) through that XCD's L2.
 #include <type_traits>
 
 #include "smoe_internal.h"
@@ -78,6 +83,7 @@ struct LdsGemmParams {
   const int32_t* n_rb;
   uint16_t* out;
   int E, H, I, Is, KT, tiles;
+  int nrb_shared;        // row blocks of the shared expert (the list's last ones)
   float limit, limit_shared;
 };
 
@@ -90,7 +96,6 @@ constexpr int kKC = 4;                // 16-wide k chunks per 64-wide stage
 constexpr int kStage = kRows * 128;   // token bytes per stage
 constexpr int kWSlots = 3;            // weight register ring slots
 constexpr int kTSlots = 2;            // LDS ring slots
-constexpr int kChunk = 32;            // consecutive work items per XCD turn
 
 __device__ inline uint32_t pack_bf16x2_l(float a, float b) {
   const __bf16 ha = (__bf16)a, hb = (__bf16)b;
@@ -210,6 +215,18 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
                            reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q))
                      : *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
   };
+  auto load_w1 = [&](u32x4 (&w)[kFR][kKC], int s, int q) {
+    const size_t off = (size_t)min(s, nst - 1) * 1024;
+#pragma unroll
+    for (int f = 0; f < kFR; ++f)
+      w[f][q] = NT ? __builtin_nontemporal_load(
+                         reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q))
+                   : *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
+  };
+  auto load_t1 = [&](u32x4 (&v)[kTL], int s, int i) {
+    const int off = min(s, nst - 1) * 64;
+    v[i] = *reinterpret_cast<const u32x4*>(tsrc[i] + off);
+  };
   auto load_t = [&](u32x4 (&v)[kTL], int s) {
     const int off = min(s, nst - 1) * 64;
 #pragma unroll
@@ -220,19 +237,28 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     for (int i = 0; i < kTL; ++i)
       *reinterpret_cast<u32x4*>(slot + (wave * kTL + i) * 1024 + lane * 16) = v[i];
   };
+  auto read_t1 = [&](const unsigned char* slot, int q, u32x4 (&t)[NA], int n) {
+    t[n] = *reinterpret_cast<const u32x4*>(slot + n * 4096 + roff[q]);
+  };
   auto read_t = [&](const unsigned char* slot, int q, u32x4 (&t)[NA]) {
 #pragma unroll
     for (int n = 0; n < NA; ++n)
       t[n] = *reinterpret_cast<const u32x4*>(slot + n * 4096 + roff[q]);
   };
-  auto mma = [&](const u32x4 (&w)[kFR][kKC], int q, const u32x4 (&t)[NA]) {
+  // one k chunk's MFMAs with hook(n) issued right after MFMA n (the
+  // scheduler keeps the order), so memory instructions interleave with them
+  auto mma_h = [&](const u32x4 (&w)[kFR][kKC], int q, const u32x4 (&t)[NA], auto hook) {
 #pragma unroll
-    for (int n = 0; n < NA; ++n)
+    for (int n = 0; n < NA; ++n) {
 #pragma unroll
       for (int f = 0; f < kFR; ++f)
         acc[f][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
             __builtin_bit_cast(bf16x8, w[f][q]), __builtin_bit_cast(bf16x8, t[n]), acc[f][n], 0,
             0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      hook(n);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   u32x4 w[kWSlots][kFR][kKC];   // weights of stages s, s+1, s+2
@@ -250,39 +276,44 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     constexpr int jw = decltype(wc)::value;   // s % 3
     constexpr int jt = decltype(tc)::value;   // s % 2
     constexpr int jw2 = (jw + 2) % kWSlots, jt1 = (jt + 1) % kTSlots;
-    load_w(w[jw2], s + 2);
-    load_t(ts[jt], s + 2);
-    __builtin_amdgcn_sched_barrier(0);
-    read_t(ring[jt], 1, t[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(w[jw], 0, t[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_t(ring[jt], 2, t[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(w[jw], 1, t[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    read_t(ring[jt], 3, t[1]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(w[jw], 2, t[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<kLoads>();
+    // stage s+1's tokens were loaded in stage s-1 before its weights: once at
+    // most those 4 kFR weight loads are outstanding, they have arrived
+    wait_vmcnt<4 * kFR>();
     write_t(ring[jt1], ts[jt1]);
+    // each chunk's MFMAs carry the next chunk's LDS reads and this stage's
+    // global loads: tokens in chunk 0, two weight loads in chunks 1 and 2
+    mma_h(w[jw], 0, t[0], [&](int n) {
+      read_t1(ring[jt], 1, t[1], n);
+#pragma unroll
+      for (int i = 0; i < kTL; ++i)
+        if (min(i, NA - 1) == n) load_t1(ts[jt], s + 2, i);
+    });
+    mma_h(w[jw], 1, t[1], [&](int n) {
+      read_t1(ring[jt], 2, t[0], n);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (min(i, NA - 1) == n) load_w1(w[jw2], s + 2, i);
+    });
+    mma_h(w[jw], 2, t[0], [&](int n) {
+      read_t1(ring[jt], 3, t[1], n);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (min(i, NA - 1) == n) load_w1(w[jw2], s + 2, 2 + i);
+    });
     lds_publish();
     __builtin_amdgcn_sched_barrier(0);
-    read_t(ring[jt1], 0, t[0]);
-    __builtin_amdgcn_sched_barrier(0);
-    mma(w[jw], 3, t[1]);
+    mma_h(w[jw], 3, t[1], [&](int n) { read_t1(ring[jt1], 0, t[0], n); });
     __builtin_amdgcn_sched_barrier(0);
   };
 
   // prologue in the same issue pattern: (W0, T0) and (W1, T1) as stages -2
   // and -1 would issue them
-  load_w(w[0], 0);
   load_t(ts[0], 0);
-  load_w(w[1], 1);
+  load_w(w[0], 0);
   load_t(ts[1], 1);
+  load_w(w[1], 1);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<kLoads>();   // stage 0's tokens have arrived
+  wait_vmcnt<kLoads + 4 * kFR>();   // stage 0's tokens have arrived
   write_t(ring[0], ts[0]);
   lds_publish();
   __builtin_amdgcn_sched_barrier(0);
@@ -400,21 +431,34 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
   auto ring = reinterpret_cast<unsigned char (*)[kStage]>(lds);
 
-  // XCD-aware deal of work items, ordered (group, weight tile, row block):
-  // the items are cut in chunks of kChunk, dealt to the 8 XCDs in turn, so
-  // the row blocks that share a weight tile and the tiles that share a row
-  // block run side by side on one XCD and meet in its L2, while the work of
-  // heavy groups (the shared expert, hot experts) spreads over all XCDs
-  const int n_items = *P.n_rb * P.tiles;
-  const int slot_b = blockIdx.x >> 3;   // this XCD's slot_b-th workgroup
-  const int item = ((slot_b / kChunk) * 8 + (blockIdx.x & 7)) * kChunk + slot_b % kChunk;
-  if (item >= n_items) return;
-  // a group's items fill [first * tiles, (first + n_group) * tiles)
-  const RowBlock any = P.rb[item / P.tiles];
-  const int local = item - any.first * P.tiles;
-  const int tile = local / any.n_group;
-  const int rbi = any.first + (local - tile * any.n_group);
-  if (rbi >= *P.n_rb) return;
+  // XCD-aware deal of work items.  Block b runs on XCD b % 8.  The routed
+  // experts' row blocks (a prefix of the list, ordered by group) are cut into
+  // 8 contiguous ranges of equal length, and so are the shared expert's; XCD
+  // x takes routed range x, then shared range x.  Inside a range the items
+  // run group by group, weight tile by weight tile, row block by row block,
+  // so the workgroups that run side by side on one XCD share an expert's
+  // weight tile (across its row blocks) and its token rows (across weight
+  // tiles) through that XCD's L2, and every XCD gets an eighth of the work.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int nrb = *P.n_rb;
+  const int n_routed = nrb - P.nrb_shared;
+  int lo = (xcd * n_routed) >> 3, hi = ((xcd + 1) * n_routed) >> 3;
+  int j = slot;
+  if (j >= (hi - lo) * P.tiles) {   // past the routed range: the shared range
+    j -= (hi - lo) * P.tiles;
+    lo = n_routed + ((xcd * P.nrb_shared) >> 3);
+    hi = n_routed + (((xcd + 1) * P.nrb_shared) >> 3);
+    if (j >= (hi - lo) * P.tiles) return;
+  }
+  // the group segment (the part of one group inside [lo, hi)) that holds
+  // item j: its items fill [(seg0 - lo) * tiles, (seg1 - lo) * tiles)
+  const RowBlock any = P.rb[lo + j / P.tiles];
+  const int seg0 = max(lo, any.first);
+  const int seg1 = min(hi, any.first + any.n_group);
+  const int local = j - (seg0 - lo) * P.tiles;
+  const int tile = local / (seg1 - seg0);
+  const int rbi = seg0 + local % (seg1 - seg0);
   const RowBlock blk = P.rb[rbi];
   const bool shared = blk.group == P.E;
   const int inter = shared ? P.Is : P.I;
@@ -432,12 +476,12 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
     lds_gemm_fragments<MODE, false>(P, blk, shared, col0, nst, ring);
 }
 
-// grid: every chunk of kChunk (row block, weight tile) items up to the
-// row-block bound gets kChunk workgroups on its XCD; 8 XCDs per turn
+// grid: 8 XCDs x the most items one XCD can receive (an eighth of the
+// row-block bound, rounded up, for the routed and for the shared experts)
 static unsigned lds_grid(const Plan& p, int tiles) {
-  const long long items = (long long)p.rb_max * tiles;
-  const long long turns = ((items + kChunk - 1) / kChunk + 7) / 8;
-  return (unsigned)(turns * 8 * kChunk);
+  const long long nrb_s = p.Is > 0 ? (p.T + p.bn - 1) / p.bn : 0;
+  const long long routed = p.rb_max - nrb_s;
+  return (unsigned)(8 * ((routed + 7) / 8 + (nrb_s + 7) / 8) * tiles);
 }
 
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s) {
@@ -446,6 +490,7 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
   gp.wa0 = a.wg; gp.wa1 = a.wu; gp.sa0 = a.sg; gp.sa1 = a.su; gp.bsrc = a.x;
   gp.row_token = a.row_token; gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.h;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.gu_tiles;
+  gp.nrb_shared = p.Is > 0 ? (p.T + p.bn - 1) / p.bn : 0;
   gp.limit = a.limit; gp.limit_shared = a.limit_shared;
   hipLaunchKernelGGL(expert_gemm_lds_kernel<0>, dim3(lds_grid(p, p.gu_tiles)), dim3(64 * kWaves), 0, s,
                      gp);
@@ -458,6 +503,7 @@ hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
   gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.o;
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.dn_tiles;
+  gp.nrb_shared = p.Is > 0 ? (p.T + p.bn - 1) / p.bn : 0;
   hipLaunchKernelGGL(expert_gemm_lds_kernel<1>, dim3(lds_grid(p, p.dn_tiles)), dim3(64 * kWaves), 0, s,
                      gp);
   return hipGetLastError();
