@@ -90,6 +90,7 @@ struct LdsGemmParams {
 namespace {
 
 constexpr int kRows = 192;            // token rows per row block at most (the plan's bn)
+constexpr int kGran = 32;             // row blocks are cut in 32-row fragments (rb_gran)
 constexpr int kFR = 1;                // 32-row weight fragments per wave
 constexpr int kWaves = 8;             // waves per workgroup: 8 x 32 = 256 weight rows
 constexpr int kKC = 4;                // 16-wide k chunks per 64-wide stage
@@ -175,20 +176,31 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   }
   // tokens: load i of this wave brings rows 8 g .. 8 g + 7 (g = wave*kTL + i),
   // 8 lanes per row; rows past the block (inside its last fragment) repeat
-  // its last row
-  const uint16_t* tsrc[kTL];
+  // its last row.  For gate/up the rows' tokens are looked up here, before
+  // the first weight loads are issued, so that the lookups and the weights
+  // travel together; the token pointers are formed after those loads.
+  int trow[kTL], tok[kTL];
 #pragma unroll
   for (int i = 0; i < kTL; ++i) {
     const int R = 8 * (wave * kTL + i) + (lane >> 3);
-    const int row = blk.row_start + min(R, blk.n_rows - 1);
-    const uint16_t* base;
-    if (MODE == 0)
-      base = P.bsrc + (size_t)P.row_token[row] * P.H;
-    else
-      base = shared ? P.bsrc + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
-                    : P.bsrc + (size_t)row * P.I;
-    tsrc[i] = base + 8 * ((lane & 7) ^ row_swizzle(R));
+    trow[i] = blk.row_start + min(R, blk.n_rows - 1);
+    if (MODE == 0) tok[i] = P.row_token[trow[i]];
   }
+  const uint16_t* tsrc[kTL];
+  auto token_pointers = [&]() {
+#pragma unroll
+    for (int i = 0; i < kTL; ++i) {
+      const int R = 8 * (wave * kTL + i) + (lane >> 3);
+      const int row = trow[i];
+      const uint16_t* base;
+      if (MODE == 0)
+        base = P.bsrc + (size_t)tok[i] * P.H;
+      else
+        base = shared ? P.bsrc + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
+                      : P.bsrc + (size_t)row * P.I;
+      tsrc[i] = base + 8 * ((lane & 7) ^ row_swizzle(R));
+    }
+  };
   // B operand of fragment n, chunk q: row R = 32 n + l31, 16-byte chunk
   // 2 q + hi of that row, at (R/8)*1024 + (R%8)*128 + (chunk ^ s(R))*16
   int roff[kKC];
@@ -306,18 +318,21 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // prologue in the same issue pattern: (W0, T0) and (W1, T1) as stages -2
-  // and -1 would issue them
-  load_t(ts[0], 0);
+  // prologue: the weights of stages 0 and 1 first (they need no token
+  // lookup), then the tokens of stages 0 and 1
   load_w(w[0], 0);
-  load_t(ts[1], 1);
   load_w(w[1], 1);
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<kLoads + 4 * kFR>();   // stage 0's tokens have arrived
+  token_pointers();
+  load_t(ts[0], 0);
+  load_t(ts[1], 1);
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<kTL>();   // stage 0's tokens have arrived (stage 1's may not)
   write_t(ring[0], ts[0]);
   lds_publish();
   __builtin_amdgcn_sched_barrier(0);
   read_t(ring[0], 0, t[0]);
+  wait_vmcnt<0>();     // stage 1's tokens, which stage 0 writes to LDS first
   int s = 0;
   for (; s + 6 <= nst; s += 6) {
     stage(ic<0>{}, ic<0>{}, s);
@@ -459,7 +474,14 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
   const int local = j - (seg0 - lo) * P.tiles;
   const int tile = local / (seg1 - seg0);
   const int rbi = seg0 + local % (seg1 - seg0);
-  const RowBlock blk = P.rb[rbi];
+  // the block itself follows from its group's rows (no second list load)
+  RowBlock blk = any;
+  {
+    int st, n;
+    split_block(any.group_rows, any.n_group, kGran, rbi - any.first, &st, &n);
+    blk.row_start = any.group_row0 + st;
+    blk.n_rows = n;
+  }
   const bool shared = blk.group == P.E;
   const int inter = shared ? P.Is : P.I;
   const int nout = (MODE == 0) ? inter : P.H;
@@ -485,7 +507,8 @@ static unsigned lds_grid(const Plan& p, int tiles) {
 }
 
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s) {
-  if (p.bn != kRows || p.H % 64 || p.I % 128 || p.Is % 128) return hipErrorInvalidValue;
+  if (p.bn != kRows || p.rb_gran != kGran || p.H % 64 || p.I % 128 || p.Is % 128)
+    return hipErrorInvalidValue;
   LdsGemmParams gp{};
   gp.wa0 = a.wg; gp.wa1 = a.wu; gp.sa0 = a.sg; gp.sa1 = a.su; gp.bsrc = a.x;
   gp.row_token = a.row_token; gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.h;
@@ -498,7 +521,8 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
 }
 
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
-  if (p.bn != kRows || p.H % 256 || p.I % 128 || p.Is % 128) return hipErrorInvalidValue;
+  if (p.bn != kRows || p.rb_gran != kGran || p.H % 256 || p.I % 128 || p.Is % 128)
+    return hipErrorInvalidValue;
   LdsGemmParams gp{};
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
   gp.rb = a.rb; gp.n_rb = a.n_rb; gp.out = a.o;

@@ -517,20 +517,6 @@ __device__ inline int block_exclusive_scan(int v, int* s_wave, int* total) {
   return ex;
 }
 
-// Block i of the n_blk = ceil(cnt / bn) row blocks of a group with cnt rows.
-// The rows are cut in whole granules of g rows (g divides bn), and the
-// blocks' granule counts differ by at most one, so every block holds at most
-// bn rows, at least one, and the last one takes the ragged end.  Blocks of
-// one group then have (nearly) the same height: the workgroups that stream
-// the same weight tile for them run at the same pace and share it in L2.
-__device__ inline void split_block(int cnt, int n_blk, int g, int i, int* start, int* n) {
-  const int F = (cnt + g - 1) / g;
-  const int q = F / n_blk, r = F % n_blk;
-  const int st = g * (i * q + min(i, r));
-  *start = st;
-  *n = min(g * (q + (i < r ? 1 : 0)), cnt - st);
-}
-
 // counts, offsets (exclusive scan) and the GEMM row-block list from one
 // expert count per thread of a 1024-thread workgroup; returns this thread's
 // offset.  Every thread must call it.
@@ -551,7 +537,7 @@ __device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int gr
       const int p = rbpos + i;
       int st, n;
       split_block(cnt, nrb, gran, i, &st, &n);
-      if (p < rb_max) rb[p] = RowBlock{tid, off + st, n, rbpos, nrb, {0, 0, 0}};
+      if (p < rb_max) rb[p] = RowBlock{tid, off + st, n, rbpos, nrb, off, cnt, 0};
     }
   }
   if (tid == 0) offsets[E] = total;
@@ -560,7 +546,7 @@ __device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int gr
     const int p = rb_total + i;
     int st, n;
     split_block(T, nrb_s, gran, i, &st, &n);
-    if (p < rb_max) rb[p] = RowBlock{E, KT + st, n, rb_total, nrb_s, {0, 0, 0}};
+    if (p < rb_max) rb[p] = RowBlock{E, KT + st, n, rb_total, nrb_s, KT, T, 0};
   }
   if (tid == 0) n_rb[0] = min(rb_total + nrb_s, rb_max);
   return off;
@@ -884,6 +870,8 @@ __global__ __launch_bounds__(256) void dense_rows_kernel(int T, int S, int bn, i
     blk.n_rows = n;
     blk.first = sl * per;
     blk.n_group = per;
+    blk.group_row0 = sl * T;
+    blk.group_rows = T;
     rb[i] = blk;
   }
   if (i == 0) *n_rb = S * per;

@@ -17,15 +17,33 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // expert-contiguous row order) that belong to `group` (an expert id, or E for
 // the shared expert), starting at global row `row_start`.  The blocks of one
 // group are consecutive in the list: `first` is the index of the group's
-// first block and `n_group` the number of its blocks.
+// first block and `n_group` the number of its blocks; the group's rows are
+// `group_rows` rows from global row `group_row0`, cut by split_block, so any
+// block of a group gives every other block of it.
 struct RowBlock {
   int32_t group;
   int32_t row_start;
   int32_t n_rows;
   int32_t first;
   int32_t n_group;
-  int32_t pad[3];
+  int32_t group_row0;
+  int32_t group_rows;
+  int32_t pad;
 };
+
+// Block i of the n_blk = ceil(cnt / bn) row blocks of a group with cnt rows.
+// The rows are cut in whole granules of g rows (g divides bn), and the
+// blocks' granule counts differ by at most one, so every block holds at most
+// bn rows, at least one, and the last one takes the ragged end.  Blocks of
+// one group then have (nearly) the same height: the workgroups that stream
+// the same weight tile for them run at the same pace.
+__device__ inline void split_block(int cnt, int n_blk, int g, int i, int* start, int* n) {
+  const int F = (cnt + g - 1) / g;
+  const int q = F / n_blk, r = F % n_blk;
+  const int st = g * (i * q + min(i, r));
+  *start = st;
+  *n = min(g * (q + (i < r ? 1 : 0)), cnt - st);
+}
 
 // ---------------------------------------------------------------- tiling plan
 // Every size the launches use is a pure function of the layer sizes, so the
