@@ -219,7 +219,7 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
             gv = fminf(gv, lim);
             uv = fminf(fmaxf(uv, -lim), lim);
           }
-          hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+          hv[j] = swiglu(gv, uv);
         }
         u32x2 pk;
         pk[0] = pack_bf16x2(hv[0], hv[1]);

@@ -381,7 +381,7 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
             gv = fminf(gv, lim);
             uv = fminf(fmaxf(uv, -lim), lim);
           }
-          hv[j] = gv / (1.0f + __expf(-gv)) * uv;
+          hv[j] = swiglu(gv, uv);
         }
         u32x2 p0, p1;
         p0[0] = pack_bf16x2_l(hv[0], hv[1]);

@@ -45,6 +45,16 @@ __device__ inline void split_block(int cnt, int n_blk, int g, int i, int* start,
   *n = min(g * (q + (i < r ? 1 : 0)), cnt - st);
 }
 
+// SwiGLU of one output, silu(g) * u with silu(g) = g / (1 + e^-g) (SiLU on
+// the gate, times the up projection).  The reciprocal is the hardware's one
+// instruction v_rcp_f32 (about 1 ulp), not a correctly rounded division (a
+// sequence of about ten): h is rounded to bf16 right after, which is 2^16
+// times coarser.  For g below about -88, e^-g overflows to infinity and the
+// result is a signed zero, as with the division.
+__device__ inline float swiglu(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // ---------------------------------------------------------------- tiling plan
 // Every size the launches use is a pure function of the layer sizes, so the
 // workspace size, the dispatch kernel and the GEMM launches agree.
