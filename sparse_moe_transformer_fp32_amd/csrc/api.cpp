@@ -633,6 +633,24 @@ moe_status moe_dense_ffn(int32_t T, int32_t H, int32_t I, int32_t S, const uint1
                 p.ws_total);
   if (T == 0) return ok();   // empty batch
   char* w = static_cast<char*>(ws);
+  if (p.nb == 1 && S <= 8) {
+    // T <= 16: two kernels, no row list and no combine (the down projection
+    // sums the slices itself)
+    uint16_t* h = reinterpret_cast<uint16_t*>(w + p.ws_h);
+    smoe::GateUpArgs ga{};
+    ga.wg = ffn->w_gate;
+    ga.wu = ffn->w_up;
+    ga.x = x;
+    ga.h = h;
+    ga.limit = swiglu_limit;
+    {
+      StageMark m(MOE_STAGE_GATE_UP, stream);
+      if ((st = launched(smoe::launch_gate_up_dense(p, ga, stream), "gate_up"))) return st;
+    }
+    StageMark m(MOE_STAGE_DOWN, stream);
+    if ((st = launched(smoe::launch_dense_down(p, ffn->w_down, h, y, stream), "down"))) return st;
+    return ok();
+  }
   int32_t* slot = reinterpret_cast<int32_t*>(w + p.ws_slot);
   {
     StageMark m(MOE_STAGE_DISPATCH, stream);

@@ -60,8 +60,9 @@ template <int KSPLIT, int FR, int NB>
 constexpr int red_slots() { return ((KSPLIT > 1) ? (4 - 4 / KSPLIT) : 1) * FR * NB * 64; }
 
 // One workgroup's tile of one row block.  MODE 0: gate/up + SwiGLU.  MODE 1:
-// down + combine weight.  NT: the weight loads are non-temporal.
-template <int MODE, int NB, int FR, int KSPLIT, int U, bool NT>
+// down + combine weight.  NT: the weight loads are non-temporal.  DENSE: the
+// row block is a whole slice of the dense FFN, whose row i is token i.
+template <int MODE, int NB, int FR, int KSPLIT, int U, bool NT, bool DENSE = false>
 __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& blk, int tile,
                                           f32x4* s_red) {
   constexpr int RG = 4 / KSPLIT;                       // row groups per workgroup
@@ -113,7 +114,8 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
   for (int nb = 0; nb < NB; ++nb) {
     const int row = blk.row_start + min(nb * 16 + r, blk.n_rows - 1);
     if (MODE == 0) {
-      bptr[nb] = P.bsrc + (size_t)P.row_token[row] * P.H + kbeg;
+      const int tok = DENSE ? row - blk.row_start : P.row_token[row];
+      bptr[nb] = P.bsrc + (size_t)tok * P.H + kbeg;
     } else {
       const uint16_t* hrow = shared ? P.bsrc + (size_t)P.KT * P.I + (size_t)(row - P.KT) * P.Is
                                     : P.bsrc + (size_t)row * P.I;
@@ -259,6 +261,115 @@ __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
     gemm_tile<MODE, NB, FR, KSPLIT, U, true>(P, blk, tile, s_red);
   else
     gemm_tile<MODE, NB, FR, KSPLIT, U, false>(P, blk, tile, s_red);
+}
+
+// Gate/up of the dense FFN for a batch of at most 16 tokens.  Slice g of
+// the intermediate dimension is group g, and its one row block holds every
+// token (row g*T + t is token t), so the row list follows from the block
+// index and no dispatch runs before it.  The weight tiles have one reader
+// each: non-temporal loads.
+__global__ __launch_bounds__(256) void dense_gate_up_kernel(GemmParams P, int T) {
+  __shared__ f32x4 s_red[red_slots<4, 2, 1>()];
+  const int tile = blockIdx.x % P.tiles;
+  const int g = blockIdx.x / P.tiles;
+  const RowBlock blk{g, g * T, T, g, 1, g * T, T, 0};
+  gemm_tile<0, 1, 2, 4, 4, true, true>(P, blk, tile, s_red);
+}
+
+// Down projection of the dense FFN for a batch of at most 16 tokens, with
+// the sum over the S slices inside the workgroup:
+//   y[t, n] = sum_s h_s[t] . Wd_s[n]
+// where h_s is slice s of the intermediate activations (rows s*T .. s*T+T-1
+// of h, I/S columns) and Wd_s the matching column slice of the down weights
+// (packed as S matrices [H, I/S]).  Wave s streams slice s's 16 weight rows
+// of the workgroup's output tile front to back (one contiguous kilobyte per
+// 32-wide k step, non-temporal: each is read once), with the same two-buffer
+// pipeline as the grouped kernel; the S partial sums meet in LDS and wave 0
+// adds them in slice order and writes y rounded once to bf16.  No o rows
+// and no combine pass.
+template <int U>
+__global__ __launch_bounds__(512) void dense_down_kernel(const uint16_t* __restrict__ wd,
+                                                         const uint16_t* __restrict__ h,
+                                                         uint16_t* __restrict__ y, int T, int H,
+                                                         int Isl) {
+  __shared__ f32x4 s_red[7 * 64];
+  const int lane = threadIdx.x & 63;
+  const int sl = threadIdx.x >> 6;                  // slice of this wave
+  const int S = blockDim.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int rt = blockIdx.x;                        // 16-row tile of the output
+  const int ksteps = Isl / 32;
+  const uint16_t* aptr = wd + (size_t)sl * H * Isl + (size_t)rt * ksteps * 512 + lane * 8;
+  // B operand: token r of slice sl (rows past the batch repeat its last one)
+  const uint16_t* bptr = h + ((size_t)sl * T + min(r, T - 1)) * Isl + 8 * g;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const int nstages = (ksteps + U - 1) / U;
+  u32x4 a0[U], b0[U], a1[U], b1[U];
+  auto load = [&](u32x4 (&a)[U], u32x4 (&b)[U], int stage) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int ks = min(stage * U + u, ksteps - 1);
+      a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(aptr + (size_t)ks * 512));
+      b[u] = *reinterpret_cast<const u32x4*>(bptr + ks * 32);
+    }
+  };
+  auto compute = [&](const u32x4 (&a)[U], const u32x4 (&b)[U], int stage) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (stage * U + u < ksteps) acc = mfma16(a[u], b[u], acc);
+  };
+  load(a0, b0, 0);
+  int st = 0;
+  for (; st + 2 < nstages; st += 2) {
+    load(a1, b1, st + 1);
+    compute(a0, b0, st);
+    load(a0, b0, st + 2);
+    compute(a1, b1, st + 1);
+  }
+  if (st + 1 < nstages) {
+    load(a1, b1, st + 1);
+    compute(a0, b0, st);
+    compute(a1, b1, st + 1);
+  } else {
+    compute(a0, b0, st);
+  }
+  // slices 1 .. S-1 park their sums; slice 0 adds them in order
+  if (sl > 0) s_red[(sl - 1) * 64 + lane] = acc;
+  __syncthreads();
+  if (sl > 0) return;
+  for (int q = 1; q < S; ++q) acc += s_red[(q - 1) * 64 + lane];
+  // lane holds output columns 16 rt + 4 g .. +3 of token r
+  if (r < T) {
+    u32x2 pk;
+    pk[0] = pack_bf16x2(acc[0], acc[1]);
+    pk[1] = pack_bf16x2(acc[2], acc[3]);
+    *reinterpret_cast<u32x2*>(y + (size_t)r * H + 16 * rt + 4 * g) = pk;
+  }
+}
+
+hipError_t launch_gate_up_dense(const Plan& p, const GateUpArgs& a, hipStream_t s) {
+  // p.E = p.K = S slices of I = p.I columns, one 16-row block per slice
+  if (p.T < 1 || p.T > 16 || p.nb != 1 || p.ksplit_gu != 4 || p.Is != 0)
+    return hipErrorInvalidValue;
+  GemmParams gp{};
+  gp.wa0 = a.wg;
+  gp.wa1 = a.wu;
+  gp.bsrc = a.x;
+  gp.out = a.h;
+  gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = 0; gp.KT = p.KT;
+  gp.tiles = p.gu_tiles;
+  gp.limit = a.limit;
+  hipLaunchKernelGGL(dense_gate_up_kernel, dim3(p.E * p.gu_tiles), dim3(256), 0, s, gp, p.T);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_down(const Plan& p, const uint16_t* wd, const uint16_t* h, uint16_t* y,
+                             hipStream_t s) {
+  if (p.T < 1 || p.T > 16 || p.E < 1 || p.E > 8 || p.H % 16 || p.I % 32)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dense_down_kernel<4>, dim3(p.H / 16), dim3(64 * p.E), 0, s, wd, h, y, p.T,
+                     p.H, p.I);
+  return hipGetLastError();
 }
 
 // --------------------------------------------------------------------------

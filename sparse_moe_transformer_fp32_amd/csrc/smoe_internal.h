@@ -129,6 +129,12 @@ struct DownArgs {
 };
 hipError_t launch_gate_up(const Plan& p, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down(const Plan& p, const DownArgs& a, hipStream_t s);
+// dense FFN at T <= 16 (plan nb == 1, p.E = p.K = S slices): gate/up with
+// the row list implied by the block index, and the down projection summed
+// over the S <= 8 slices in the workgroup, written straight to y
+hipError_t launch_gate_up_dense(const Plan& p, const GateUpArgs& a, hipStream_t s);
+hipError_t launch_dense_down(const Plan& p, const uint16_t* wd, const uint16_t* h, uint16_t* y,
+                             hipStream_t s);
 // large row blocks (plan nb == 12): LDS-pipelined variants
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s);
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s);

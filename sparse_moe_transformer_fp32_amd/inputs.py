@@ -186,13 +186,15 @@ DENSE_WORKLOADS: Dict[str, DenseWorkload] = {
 }
 
 
-def make_dense_inputs(wl: DenseWorkload, device: str = "cpu", T: Optional[int] = None):
+def make_dense_inputs(wl: DenseWorkload, device: str = "cpu", T: Optional[int] = None,
+                      seed: Optional[int] = None):
     """x [T,H] bf16 (rows at unit RMS), Wg, Wu [I,H] and Wd [H,I] bf16 from
-    one generator seeded once, drawn in that order."""
+    one generator seeded once (with the workload's seed unless `seed` is
+    given), drawn in that order."""
     T = wl.T if T is None else T
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
-    gen.manual_seed(wl.seed)
+    gen.manual_seed(wl.seed if seed is None else seed)
     x = _unit_rms_rows(_normal(gen, (T, wl.H), 1.0, dev)).to(torch.bfloat16)
     wg = _normal(gen, (wl.I, wl.H), wl.w_std, dev).to(torch.bfloat16)
     wu = _normal(gen, (wl.I, wl.H), wl.w_std, dev).to(torch.bfloat16)

@@ -451,6 +451,11 @@ DENSE = {  # name: (seed, T, H, I, S)
     "lds_S4": (153, 300, 512, 1024, 4),
     "lds_ragged_S8": (154, 777, 256, 2048, 8),
     "fallback_S16": (155, 100, 256, 1024, 16),
+    # T <= 16 and S <= 8: two-kernel path (slice sum inside the down kernel)
+    "two_kernel_T13_S8": (156, 13, 512, 2048, 8),
+    "two_kernel_T16_S2": (157, 16, 384, 768, 2),
+    # T <= 16 with S > 8: the row list, the grouped kernels and the combine
+    "small_T8_S16": (158, 8, 256, 1024, 16),
 }
 
 
