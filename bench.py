@@ -313,6 +313,38 @@ def read_ceiling(gib: int = 4, reps: int = 10):
     return out
 
 
+def short_read_ceiling(mibs=(88, 176, 264), reps=40):
+    """HBM read rate of short non-temporal reads (moe_read_probe), the sizes
+    of the dense decode FFN's down weights, gate/up weights and whole layer:
+    the median of `reps` single reads timed with HIP events, each of a
+    different buffer of a rotation of over 1 GiB, so that no read finds its
+    data in the 256 MB last-level cache.  The floor of a kernel that streams
+    that many bytes once, launch included."""
+    import torch
+    from sparse_moe_transformer_fp32_amd import binding as B
+    sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    out = {}
+    for mib in mibs:
+        nb = mib << 20
+        bufs = [torch.ones(nb, dtype=torch.uint8, device="cuda") for _ in range(1100 // mib + 2)]
+        for i in range(3):
+            B.read_probe(bufs[i], sink, True)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for i, (a, b) in enumerate(ev):
+            a.record()
+            B.read_probe(bufs[i % len(bufs)], sink, True)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        out[f"{mib}MiB"] = {"us_per_read": round(ms * 1e3, 1),
+                            "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
+                            "frac_of_8tbs": round(nb / (ms * 1e-3) / 8e12, 3)}
+        del bufs
+        torch.cuda.empty_cache()
+    return out
+
+
 def layer_work(wl, counts):
     """Algorithmic bytes and FLOPs of one layer call, and of its gate/up
     kernel, from the measured expert counts."""
@@ -634,6 +666,9 @@ def main():
     ap.add_argument("--read-ceiling", action="store_true",
                     help="only measure the HBM read rate of a plain 4 GiB read (moe_read_probe) "
                          "with ordinary and with non-temporal loads, and exit")
+    ap.add_argument("--short-read-ceiling", action="store_true",
+                    help="only measure short non-temporal reads of 88, 176 and 264 MiB "
+                         "(the dense decode FFN's weight streams) on rotating buffers")
     ap.add_argument("--no-read-ceiling", action="store_true",
                     help="skip the HBM read-ceiling side measurement of the default run")
     ap.add_argument("--no-dense", action="store_true",
@@ -682,6 +717,9 @@ def main():
         return
     if args.library_reference:
         print(json.dumps({"library_reference": library_reference()}), flush=True)
+        return
+    if args.short_read_ceiling:
+        print(json.dumps({"short_read_ceiling": short_read_ceiling()}), flush=True)
         return
     if args.read_ceiling:
         print(json.dumps({"read_ceiling": read_ceiling()}), flush=True)

@@ -322,9 +322,11 @@ size_t moe_dense_workspace_bytes(int32_t T, int32_t H, int32_t I, int32_t S);
  * 方法, and paperlayer.ai summary, §2.2: the first three of the 45 layers
  * are dense; model card: intermediate_size 11264).  The intermediate
  * dimension is cut into S slices that run as S groups of the grouped
- * expert GEMMs, every token in every group with weight 1; the S partial
- * outputs of a token are rounded to bf16 and added in fp32 in slice order,
- * then rounded once more.
+ * expert GEMMs, every token in every group with weight 1.  For T <= 16 and
+ * S <= 8 the down projection adds the S slices' fp32 partial sums in slice
+ * order and rounds y once to bf16; otherwise the S partial outputs of a
+ * token are rounded to bf16 and added in fp32 in slice order, then rounded
+ * once more.
  *   T, H     as in moe_dims
  *   I        intermediate size; I/S must be a multiple of 64, <= 16384
  *   S        slices, 1 <= S <= 16; T*S <= 1<<24.  w_down must have been
