@@ -98,6 +98,7 @@ KERNEL_SOURCES = {
     "decode": [_CSRC + "expert_gemm.hip", _CSRC + "api.cpp", _CSRC + "smoe_internal.h"],
     "prefill": [_CSRC + "expert_gemm_lds.hip", _CSRC + "api.cpp", _CSRC + "smoe_internal.h"],
 }
+KERNEL_SOURCES["dense_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["long"] = KERNEL_SOURCES["skew"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["skew_mild"] = KERNEL_SOURCES["prefill"]
 
@@ -164,6 +165,7 @@ def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
 # the gate/up kernel each counter workload launches (decode: register-streaming;
 # prefill: LDS-pipelined)
 GATE_UP_KERNEL = {"decode": "void smoe::expert_gemm_kernel<0,",
+                  "dense_decode": "smoe::dense_gate_up_kernel",
                   "prefill": "void smoe::expert_gemm_lds_kernel<0>",
                   "long": "void smoe::expert_gemm_lds_kernel<0>",
                   "skew": "void smoe::expert_gemm_lds_kernel<0>"}
@@ -193,7 +195,7 @@ def write_traffic(pmc_root, commands):
             f"# a plain 1 GiB device copy: FETCH_SIZE read {cf:.0f} KiB -> factor {f_fetch:.4f};",
             f"# WRITE_SIZE read {cw:.0f} KiB -> factor {f_write:.4f}.", "# commands:"]
     head += [f"#   {c}" for c in commands]
-    for wl in ("decode", "prefill", "long", "skew"):
+    for wl in ("decode", "prefill", "long", "skew", "dense_decode"):
         if not os.path.isdir(os.path.join(pmc_root, f"{wl}_FETCH_SIZE")):
             continue
         fe, wr = per_kernel(wl, "FETCH_SIZE"), per_kernel(wl, "WRITE_SIZE")
@@ -490,6 +492,10 @@ def run_dense_bench(name, steps, warmup, device="cuda"):
             "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "gate_up_tflops": round(2 * T * 2 * H * I / (gu_ms * 1e-3) / 1e12, 2),
+            # HBM bytes of the gate/up kernel per launch (rocprofv3 counters,
+            # committed; null once its sources changed) against 2*H*I*2 B
+            "gate_up_bytes": {"algorithmic": 2 * H * I * 2,
+                              "traffic": _traffic("gate_up:dense_decode") if T <= 16 else None},
             "down_tflops": round(2 * T * H * I / (dn_ms * 1e-3) / 1e12, 2),
             "stage_ms": {k: round(v, 4) for k, v in st.items() if v > 0}}
 
