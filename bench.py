@@ -315,6 +315,38 @@ def read_ceiling(gib: int = 4, reps: int = 10):
     return out
 
 
+def mfma_ceiling(iters: int = 65536, reps: int = 5):
+    """The bf16 matrix-core rate the chip sustains with no memory traffic
+    (moe_mfma_probe: one 8-wave workgroup per CU, four independent
+    32x32x16 MFMA chains per wave), the best of `reps` timed launches after
+    two untimed ones, and the shader clock it ran at (the probe's s_memtime
+    and 100 MHz s_memrealtime counts over its loop).  The practical ceiling
+    of the grouped GEMMs' MFMA figures, next to the nominal 2.5 PF."""
+    import torch
+    from sparse_moe_transformer_fp32_amd import binding as B
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clocks = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        B.mfma_probe(iters, clocks, sink)
+    best, clk = None, None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        B.mfma_probe(iters, clocks, sink)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        if best is None or ms < best:
+            c = clocks.view(cus, 2).double().sum(0).tolist()
+            best, clk = ms, c[0] / c[1] * 0.1   # GHz: shader ticks per 100 MHz tick
+    flops = cus * 8 * iters * 4 * 32768
+    tf = flops / (best * 1e-3) / 1e12
+    return {"iters": iters, "ms": round(best, 4), "tflops": round(tf, 1),
+            "frac_of_2500": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "clock_ghz": round(clk, 3),
+            "frac_of_clock_peak": round(tf / (cus * 4 * 1024 * clk * 1e9 / 1e12), 4)}
+
+
 def short_read_ceiling(mibs=(88, 176, 264), reps=40):
     """HBM read rate of short non-temporal reads (moe_read_probe), the sizes
     of the dense decode FFN's down weights, gate/up weights and whole layer:
@@ -672,6 +704,11 @@ def main():
     ap.add_argument("--read-ceiling", action="store_true",
                     help="only measure the HBM read rate of a plain 4 GiB read (moe_read_probe) "
                          "with ordinary and with non-temporal loads, and exit")
+    ap.add_argument("--mfma-ceiling", action="store_true",
+                    help="only measure the bf16 matrix-core rate with no memory traffic "
+                         "(moe_mfma_probe) and the clock it runs at")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the matrix-core ceiling side measurement of the default run")
     ap.add_argument("--short-read-ceiling", action="store_true",
                     help="only measure short non-temporal reads of 88, 176 and 264 MiB "
                          "(the dense decode FFN's weight streams) on rotating buffers")
@@ -723,6 +760,9 @@ def main():
         return
     if args.library_reference:
         print(json.dumps({"library_reference": library_reference()}), flush=True)
+        return
+    if args.mfma_ceiling:
+        print(json.dumps({"mfma_ceiling": mfma_ceiling()}), flush=True)
         return
     if args.short_read_ceiling:
         print(json.dumps({"short_read_ceiling": short_read_ceiling()}), flush=True)
@@ -818,6 +858,16 @@ def main():
         if not args.no_skew:
             line["skew"] = side_layer_obj("skew", side_steps, 3)
             torch.cuda.empty_cache()
+        if not args.no_mfma_ceiling:
+            # the sustained matrix-core rate, next to the nominal 2.5 PF the
+            # GEMM rooflines use
+            mc = mfma_ceiling()
+            line["mfma_ceiling"] = mc
+            for name in ("prefill", "long", "skew"):
+                if name in line:
+                    for g in ("roofline_gate_up", "roofline_down"):
+                        line[name][g + "_over_mfma_ceiling"] = round(
+                            line[name][g]["achieved"] / mc["tflops"], 4)
     print(json.dumps(line), flush=True)
 
 

@@ -381,6 +381,23 @@ moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events);
 moe_status moe_read_probe(const void* buf, size_t bytes, int32_t nontemporal, void* sink,
                           hipStream_t stream);
 
+/* Measurement aid, not part of the layer: the bf16 matrix-core rate the
+ * chip sustains on work without memory traffic, the practical ceiling the
+ * GEMMs' MFMA figures are compared with next to the nominal peak.  One
+ * workgroup of 8 waves (two per SIMD) on each compute unit; each wave runs
+ * `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 on register
+ * operands: CUs x 8 x iters x 4 x 32768 FLOPs, enqueued on `stream`.
+ * `clocks` (device, n_clocks >= 2 x the CU count uint64 values) receives for
+ * each workgroup the shader clock counter (s_memtime) and the 100 MHz
+ * real-time counter (s_memrealtime) elapsed over its loop: their ratio
+ * times 100 MHz is the clock the matrix cores ran at.  `sink` (16 bytes,
+ * device) is written only in a case that does not occur.  Returns
+ * MOE_ERR_NULL, MOE_ERR_ALIGN (clocks or sink not 16-byte aligned),
+ * MOE_ERR_SHAPE (iters outside [1, 1 << 24], or n_clocks too small), or
+ * MOE_ERR_DEVICE (device query or launch failed). */
+moe_status moe_mfma_probe(int32_t iters, uint64_t* clocks, int32_t n_clocks, void* sink,
+                          hipStream_t stream);
+
 /* For callers that cannot allocate: code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc.  moe_forward with the
  * same arguments minus the workspace: the scratch memory comes from a fixed

@@ -29,7 +29,7 @@ EXPORTED = ["moe_abi_version", "moe_last_error", "moe_workspace_bytes", "moe_wor
             "moe_route", "moe_forward", "moe_forward_residual", "moe_residual_rmsnorm",
             "moe_set_stage_events", "moe_pack_weights", "moe_pack_weights_strided",
             "moe_dense_workspace_bytes", "moe_dense_ffn", "moe_expert_stats", "moe_read_probe",
-            "moe_forward_noalloc"]
+            "moe_mfma_probe", "moe_forward_noalloc"]
 # bytes of the library's fixed scratch array (moe_forward_noalloc)
 NOALLOC_SCRATCH_BYTES = 32 << 20
 STAGES = ["route_logits", "route_topk", "dispatch", "gate_up", "down", "combine"]
@@ -140,6 +140,8 @@ def load() -> ctypes.CDLL:
     lib.moe_set_stage_events.argtypes = [_vp, ctypes.c_int32]
     lib.moe_read_probe.restype = ctypes.c_int
     lib.moe_read_probe.argtypes = [_vp, ctypes.c_size_t, ctypes.c_int32, _vp, _vp]
+    lib.moe_mfma_probe.restype = ctypes.c_int
+    lib.moe_mfma_probe.argtypes = [ctypes.c_int32, _vp, ctypes.c_int32, _vp, _vp]
     v = lib.moe_abi_version()
     if v != ABI_VERSION:
         raise RuntimeError(f"{LIB_PATH}: ABI version {v}, binding expects {ABI_VERSION}")
@@ -490,6 +492,17 @@ def read_probe(buf: torch.Tensor, sink: torch.Tensor, nontemporal: bool) -> None
     lib = load()
     _check(lib.moe_read_probe(_vp(buf.data_ptr()), buf.numel() * buf.element_size(),
                               1 if nontemporal else 0, _vp(sink.data_ptr()), _stream(buf.device)))
+
+
+def mfma_probe(iters: int, clocks: torch.Tensor, sink: torch.Tensor) -> None:
+    """iters rounds of four bf16 32x32x16 MFMAs per wave, one 8-wave
+    workgroup per CU, on the current stream (moe_mfma_probe): the matrix-core
+    rate the chip sustains.  `clocks` is an int64 device tensor of at least
+    2 x CU-count entries that receives each workgroup's (shader clock ticks,
+    100 MHz ticks) over its loop; `sink` a 16-byte device tensor."""
+    lib = load()
+    _check(lib.moe_mfma_probe(iters, _vp(clocks.data_ptr()), clocks.numel(), _vp(sink.data_ptr()),
+                              _stream(clocks.device)))
 
 
 def residual_rmsnorm(r_in: torch.Tensor, y_add: Optional[torch.Tensor] = None,

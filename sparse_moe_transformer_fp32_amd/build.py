@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsmoe_gfx950.so")
 
 SOURCES = ["route.hip", "expert_gemm.hip", "expert_gemm_lds.hip", "combine.hip", "pack.hip",
-           "stats.hip", "read_probe.hip",
+           "stats.hip", "read_probe.hip", "mfma_probe.hip",
            "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

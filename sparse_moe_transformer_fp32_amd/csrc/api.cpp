@@ -738,6 +738,30 @@ moe_status moe_read_probe(const void* buf, size_t bytes, int32_t nontemporal, vo
   return ok();
 }
 
+moe_status moe_mfma_probe(int32_t iters, uint64_t* clocks, int32_t n_clocks, void* sink,
+                          hipStream_t stream) {
+  if (!clocks || !sink) return fail(MOE_ERR_NULL, "moe_mfma_probe: NULL clocks or sink");
+  if (misaligned(clocks) || misaligned(sink))
+    return fail(MOE_ERR_ALIGN, "moe_mfma_probe: clocks and sink must be 16-byte aligned");
+  if (iters < 1 || iters > (1 << 24))
+    return fail(MOE_ERR_SHAPE, "moe_mfma_probe: iters=%d out of range [1, 16777216]", iters);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess)
+    return fail(MOE_ERR_DEVICE, "moe_mfma_probe: device query failed: %s", hipGetErrorString(e));
+  if (n_clocks < 2 * cus)
+    return fail(MOE_ERR_SHAPE, "moe_mfma_probe: n_clocks=%d < 2 x %d compute units", n_clocks,
+                cus);
+  moe_status st;
+  if ((st = launched(smoe::launch_mfma_probe(iters, cus,
+                                             reinterpret_cast<unsigned long long*>(clocks), sink,
+                                             stream),
+                     "mfma_probe")))
+    return st;
+  return ok();
+}
+
 moe_status moe_set_stage_events(hipEvent_t* events, int32_t n_events) {
   if (!events) {
     g_stage_events = nullptr;

@@ -142,6 +142,9 @@ hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s);
 // counts[0..E) = 0 and offsets[0..E] = 0 (the routing of an empty batch)
 hipError_t launch_read_probe(const void* buf, size_t bytes, bool nontemporal, void* sink,
                              hipStream_t s);
+// one workgroup of 8 waves on each of `grid` CUs, `iters` rounds of 4 MFMAs
+hipError_t launch_mfma_probe(int iters, int grid, unsigned long long* clocks, void* sink,
+                             hipStream_t s);
 hipError_t launch_zero_counts(int32_t* counts, int32_t* offsets, int E, hipStream_t s);
 
 hipError_t launch_pack(const uint16_t* src, uint16_t* dst, int n_mats, int rows, int cols,

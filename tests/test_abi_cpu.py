@@ -343,6 +343,18 @@ def test_empty_batch_host_paths():
                                 None) == B.MOE_ERR_SHAPE
 
 
+def test_mfma_probe_checks():
+    """moe_mfma_probe rejects bad arguments on the host, before any HIP call."""
+    lib = B.load()
+    assert lib.moe_mfma_probe(16, None, 512, _vp(A), None) == B.MOE_ERR_NULL
+    assert lib.moe_mfma_probe(16, _vp(A), 512, None, None) == B.MOE_ERR_NULL
+    assert lib.moe_mfma_probe(16, _vp(A + 8), 512, _vp(A), None) == B.MOE_ERR_ALIGN
+    assert lib.moe_mfma_probe(16, _vp(A), 512, _vp(A + 4), None) == B.MOE_ERR_ALIGN
+    assert lib.moe_mfma_probe(0, _vp(A), 512, _vp(A), None) == B.MOE_ERR_SHAPE
+    assert lib.moe_mfma_probe((1 << 24) + 1, _vp(A), 512, _vp(A), None) == B.MOE_ERR_SHAPE
+    assert "iters" in B.last_error()
+
+
 def test_read_probe_checks():
     """moe_read_probe rejects bad arguments on the host, before any HIP call."""
     lib = B.load()

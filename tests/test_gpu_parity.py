@@ -710,3 +710,20 @@ def test_read_probe_reads_without_writing():
         B.read_probe(buf, sink, nt)
     torch.cuda.synchronize()
     assert int(sink.sum()) == 0
+
+
+def test_mfma_probe_runs_on_every_cu():
+    """The matrix-core ceiling probe: every CU's workgroup reports its loop's
+    shader-clock and real-time counts, the clock they give lies in a
+    physical range, and the sink is untouched."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    clocks = torch.zeros(2 * cus, dtype=torch.int64, device="cuda")
+    sink = torch.zeros(4, dtype=torch.float32, device="cuda")
+    B.mfma_probe(4096, clocks, sink)
+    torch.cuda.synchronize()
+    c = clocks.view(cus, 2).cpu().numpy().astype(np.float64)
+    assert (c > 0).all(), c
+    ghz = c[:, 0].sum() / c[:, 1].sum() * 0.1
+    print(f"mfma probe: {cus} CUs, clock {ghz:.3f} GHz", flush=True)
+    assert 0.3 < ghz < 3.5, ghz
+    assert float(sink.abs().sum()) == 0.0
