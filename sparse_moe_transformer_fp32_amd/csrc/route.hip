@@ -549,6 +549,7 @@ __device__ inline int finish_counts(int cnt, int E, int T, int K, int bn, int gr
     if (p < rb_max) rb[p] = RowBlock{E, KT + st, n, rb_total, nrb_s, KT, T, 0};
   }
   if (tid == 0) n_rb[0] = min(rb_total + nrb_s, rb_max);
+  if (tid == 1 || tid == 2) n_rb[tid] = 0;   // the GEMMs' pool claim counters
   return off;
 }
 
@@ -875,6 +876,7 @@ __global__ __launch_bounds__(256) void dense_rows_kernel(int T, int S, int bn, i
     rb[i] = blk;
   }
   if (i == 0) *n_rb = S * per;
+  if (i == 1 || i == 2) n_rb[i] = 0;   // the GEMMs' pool claim counters
 }
 
 hipError_t launch_dense_rows(const Plan& p, int32_t* row_token, float* row_w, int32_t* slot_pos,
