@@ -107,6 +107,9 @@ constexpr int kTSlots = 2;            // LDS ring slots
 // latency and the lost L2 locality cost more than the balance gains.
 template <int MODE>
 constexpr int pool_pct() { return MODE == 0 ? 5 : 0; }
+// claimer slots per XCD, in multiples of its own pool share (each claimer
+// that finds the pool empty costs a workgroup launch)
+constexpr int kPoolRoom = 3;
 
 __device__ inline uint32_t pack_bf16x2_l(float a, float b) {
   const __bf16 ha = (__bf16)a, hb = (__bf16)b;
@@ -466,7 +469,7 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
   // tiles) through that XCD's L2, and every XCD gets an eighth of the work.
   // The last pool_pct() percent of each XCD's items are claimed from a
   // common pool by the workgroups past their XCD's own items (the grid has
-  // room for any XCD to claim the whole pool; the claim counter is zeroed
+  // room for an XCD to claim three times its share; the claim counter is zeroed
   // by the dispatch).  Which CU runs an item does not change its result.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
@@ -548,8 +551,8 @@ static unsigned lds_grid(const Plan& p, int tiles, int pct) {
   const long long nrb_s = p.Is > 0 ? (p.T + p.bn - 1) / p.bn : 0;
   const long long routed = p.rb_max - nrb_s;
   const long long per_xcd = ((routed + 7) / 8 + (nrb_s + 7) / 8) * tiles;
-  // room for every XCD to claim the whole pool
-  return (unsigned)(8 * (per_xcd + 8 * (per_xcd * pct / 100)));
+  // room for every XCD to claim kPoolRoom times its own share of the pool
+  return (unsigned)(8 * (per_xcd + kPoolRoom * (per_xcd * pct / 100)));
 }
 
 hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s) {
