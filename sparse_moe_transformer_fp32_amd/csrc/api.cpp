@@ -256,10 +256,11 @@ void make_plan(int T, int H, int E, int K, int I, int Is, Plan* p) {
     p->ksplit_gu = p->ksplit_dn = 1;
     p->gu_rows_wg = 64;
     p->dn_rows_wg = 128;
-  } else {  // LDS-pipelined kernels: 128 gate/up columns or 256 down rows
+  } else {  // LDS-pipelined kernels: 128 gate/up columns; 512 down rows
+            // (256 when H is not a multiple of 512)
     p->ksplit_gu = p->ksplit_dn = 1;
     p->gu_rows_wg = 128;
-    p->dn_rows_wg = 256;
+    p->dn_rows_wg = H % 512 == 0 ? 512 : 256;
   }
   p->gu_tiles = std::max(I, Is) / p->gu_rows_wg;
   p->dn_tiles = H / p->dn_rows_wg;

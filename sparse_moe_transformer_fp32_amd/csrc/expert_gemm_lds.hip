@@ -22,6 +22,12 @@
 // columns, so accumulator registers j and j+8 of a lane are the gate and up
 // values of one output and SwiGLU happens in registers.
 //
+// Down work items cover 512 output rows (when H allows): a row block of at
+// most 128 tokens runs them as one tile of two weight fragments per wave
+// (512 x 128: twice the weight bytes per item for the same fixed prologue
+// and epilogue, which are a quarter of a 256-row down item at that height),
+// a taller block as two 256-row passes one after the other.
+//
 // Pipeline, one 64-wide k stage per step:
 //  - Tokens (shared by the 8 waves) are gathered with full-line loads: one
 //    load instruction moves 8 rows x 128 bytes (8 lanes per row) into
@@ -86,18 +92,36 @@ struct LdsGemmParams {
   int nrb_shared;        // row blocks of the shared expert (the list's last ones)
   float limit, limit_shared;
   int* pool;             // claim counter of the pooled items (zeroed by the dispatch)
+  int wide;              // down: 512-row items (else 256)
 };
 
 namespace {
 
 constexpr int kRows = 192;            // token rows per row block at most (the plan's bn)
 constexpr int kGran = 32;             // row blocks are cut in 32-row fragments (rb_gran)
-constexpr int kFR = 1;                // 32-row weight fragments per wave
-constexpr int kWaves = 8;             // waves per workgroup: 8 x 32 = 256 weight rows
+constexpr int kWaves = 8;             // waves per workgroup
 constexpr int kKC = 4;                // 16-wide k chunks per 64-wide stage
-constexpr int kStage = kRows * 128;   // token bytes per stage
-constexpr int kWSlots = 3;            // weight register ring slots
 constexpr int kTSlots = 2;            // LDS ring slots
+
+// The shape of one work item: FR 32-row weight fragments per wave (8 x 32 FR
+// weight rows per workgroup), at most ROWS tokens, a WS-slot weight register
+// ring.  kStage is the bytes of one LDS ring slot: what the waves' token
+// loads bring, 8 rows a load and ceil(NA/2) loads a wave.
+template <int FR, int ROWS, int WS>
+struct TileShape {
+  static constexpr int kFR = FR;
+  static constexpr int kRows = ROWS;
+  static constexpr int kWSlots = WS;
+  static constexpr int kMaxNA = ROWS / 32;
+  static constexpr int kStage = kWaves * ((kMaxNA * 4 + kWaves - 1) / kWaves) * 8 * 128;
+};
+// 256 weight rows x up to 192 tokens, one fragment per wave, a 3-slot ring
+typedef TileShape<1, 192, 3> TileA;
+// 512 weight rows x up to 128 tokens, two fragments per wave: twice the
+// weight bytes per item for the same fixed prologue and epilogue; a stage
+// is twice as long, so a 2-slot ring keeps as much time in flight (and the
+// registers within 256).  Used for the down items of at most 128 rows.
+typedef TileShape<2, 128, 2> TileW;
 // Share (%) of each XCD's items that go to a common pool, per GEMM.  The
 // XCDs get equal shares of the work but do not run at equal speed, so the
 // kernel ends when the slowest XCD does; workgroups past their XCD's own
@@ -148,14 +172,25 @@ __device__ inline int row_swizzle(int R) { return (R >> 1) & 7; }
 template <int I>
 using ic = std::integral_constant<int, I>;
 
+// f(ic<B>{}), f(ic<B + 1>{}), ..., f(ic<E - 1>{}), unrolled at compile time
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(ic<B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
 }  // namespace
 
 // The pipelined K loop and the epilogue for one work item whose row block
 // has NA 32-token fragments with real rows.
-template <int MODE, int NA, bool NT>
+template <int MODE, int NA, bool NT, typename TS>
 __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowBlock& blk,
                                               bool shared, int col0, int nst,
-                                              unsigned char (*ring)[kStage]) {
+                                              unsigned char (*ring)[TS::kStage]) {
+  constexpr int kFR = TS::kFR;
+  constexpr int kWSlots = TS::kWSlots;
   // token loads per wave per stage (8 rows each): the 8 waves bring the
   // 32 NA rows of the fragments in use (for odd NA the last loads repeat the
   // block's last row into LDS rows no fragment reads)
@@ -286,7 +321,7 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
     }
   };
 
-  u32x4 w[kWSlots][kFR][kKC];   // weights of stages s, s+1, s+2
+  u32x4 w[kWSlots][kFR][kKC];   // weights of stages s .. s + kWSlots - 1
   u32x4 ts[2][kTL];              // tokens of stages s+1, s+2 on their way to LDS
   u32x4 t[2][NA];                // B operands of the current and the next k chunk
   // Stage s (weight slot s%3, token staging buffer and LDS slot s%2) first
@@ -298,9 +333,9 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   // waves have passed).  The barrier after lgkmcnt(0) publishes them for the
   // first chunk of s+1.
   auto stage = [&](auto wc, auto tc, int s) {
-    constexpr int jw = decltype(wc)::value;   // s % 3
+    constexpr int jw = decltype(wc)::value;   // s % kWSlots
     constexpr int jt = decltype(tc)::value;   // s % 2
-    constexpr int jw2 = (jw + 2) % kWSlots, jt1 = (jt + 1) % kTSlots;
+    constexpr int jw2 = (jw + kWSlots - 1) % kWSlots, jt1 = (jt + 1) % kTSlots;
     // stage s+1's tokens were loaded in stage s-1 before its weights: once at
     // most those 4 kFR weight loads are outstanding, they have arrived
     wait_vmcnt<4 * kFR>();
@@ -317,13 +352,13 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
       read_t1(ring[jt], 2, t[0], n);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (min(i, NA - 1) == n) load_w1(w[jw2], s + 2, i);
+        if (min(i, NA - 1) == n) load_w1(w[jw2], s + kWSlots - 1, i);
     });
     mma_h(w[jw], 2, t[0], [&](int n) {
       read_t1(ring[jt], 3, t[1], n);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (min(i, NA - 1) == n) load_w1(w[jw2], s + 2, 2 + i);
+        if (min(i, NA - 1) == n) load_w1(w[jw2], s + kWSlots - 1, 2 + i);
     });
     lds_publish();
     __builtin_amdgcn_sched_barrier(0);
@@ -333,8 +368,8 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
 
   // prologue: the weights of stages 0 and 1 first (they need no token
   // lookup), then the tokens of stages 0 and 1
-  load_w(w[0], 0);
-  load_w(w[1], 1);
+#pragma unroll
+  for (int k = 0; k + 1 < kWSlots; ++k) load_w(w[k], k);
   __builtin_amdgcn_sched_barrier(0);
   token_pointers();
   load_t(ts[0], 0);
@@ -346,21 +381,19 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   __builtin_amdgcn_sched_barrier(0);
   read_t(ring[0], 0, t[0]);
   wait_vmcnt<0>();     // stage 1's tokens, which stage 0 writes to LDS first
+  // the slot pair (s % kWSlots, s % 2) repeats every kPer stages
+  constexpr int kPer = (kWSlots % 2) ? 2 * kWSlots : kWSlots;
   int s = 0;
-  for (; s + 6 <= nst; s += 6) {
-    stage(ic<0>{}, ic<0>{}, s);
-    stage(ic<1>{}, ic<1>{}, s + 1);
-    stage(ic<2>{}, ic<0>{}, s + 2);
-    stage(ic<0>{}, ic<1>{}, s + 3);
-    stage(ic<1>{}, ic<0>{}, s + 4);
-    stage(ic<2>{}, ic<1>{}, s + 5);
-  }
+  for (; s + kPer <= nst; s += kPer)
+    static_for<0, kPer>([&](auto k) {
+      constexpr int K = decltype(k)::value;
+      stage(ic<K % kWSlots>{}, ic<K % 2>{}, s + K);
+    });
   // tail: the remaining stages continue the same slot sequence
-  if (s < nst) stage(ic<0>{}, ic<0>{}, s);
-  if (s + 1 < nst) stage(ic<1>{}, ic<1>{}, s + 1);
-  if (s + 2 < nst) stage(ic<2>{}, ic<0>{}, s + 2);
-  if (s + 3 < nst) stage(ic<0>{}, ic<1>{}, s + 3);
-  if (s + 4 < nst) stage(ic<1>{}, ic<0>{}, s + 4);
+  static_for<0, kPer - 1>([&](auto k) {
+    constexpr int K = decltype(k)::value;
+    if (s + K < nst) stage(ic<K % kWSlots>{}, ic<K % 2>{}, s + K);
+  });
   wait_vmcnt<0>();
 
   // epilogue: accumulator register j of a lane is weight row
@@ -436,28 +469,54 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
   }
 }
 
-// the item's body for its number of 32-token fragments with rows
+// The item's body for its number of 32-token fragments with rows.  Gate/up
+// items are 256 weight rows (128 outputs).  Down items are 512 output rows
+// when H allows (P.wide): one 512-row pass when the block has at most 128
+// rows, else two 256-row passes one after the other; otherwise 256 rows.
+template <int MODE, bool NT, typename TS>
+__device__ __forceinline__ void lds_gemm_na(const LdsGemmParams& P, const RowBlock& blk, bool shared,
+                                            int col0, int nst, unsigned char* lds) {
+  auto ring = reinterpret_cast<unsigned char (*)[TS::kStage]>(lds);
+  switch ((blk.n_rows + 31) >> 5) {
+    case 1: lds_gemm_item<MODE, 1, NT, TS>(P, blk, shared, col0, nst, ring); break;
+    case 2: lds_gemm_item<MODE, 2, NT, TS>(P, blk, shared, col0, nst, ring); break;
+    case 3: lds_gemm_item<MODE, 3, NT, TS>(P, blk, shared, col0, nst, ring); break;
+    case 4: lds_gemm_item<MODE, 4, NT, TS>(P, blk, shared, col0, nst, ring); break;
+    case 5:
+      if constexpr (TS::kMaxNA >= 5) lds_gemm_item<MODE, 5, NT, TS>(P, blk, shared, col0, nst, ring);
+      break;
+    default:
+      if constexpr (TS::kMaxNA >= 6) lds_gemm_item<MODE, 6, NT, TS>(P, blk, shared, col0, nst, ring);
+      break;
+  }
+}
+
 template <int MODE, bool NT>
 __device__ __forceinline__ void lds_gemm_fragments(const LdsGemmParams& P, const RowBlock& blk,
                                                    bool shared, int col0, int nst,
-                                                   unsigned char (*ring)[kStage]) {
-  switch ((blk.n_rows + 31) >> 5) {
-    case 1: lds_gemm_item<MODE, 1, NT>(P, blk, shared, col0, nst, ring); break;
-    case 2: lds_gemm_item<MODE, 2, NT>(P, blk, shared, col0, nst, ring); break;
-    case 3: lds_gemm_item<MODE, 3, NT>(P, blk, shared, col0, nst, ring); break;
-    case 4: lds_gemm_item<MODE, 4, NT>(P, blk, shared, col0, nst, ring); break;
-    case 5: lds_gemm_item<MODE, 5, NT>(P, blk, shared, col0, nst, ring); break;
-    default: lds_gemm_item<MODE, 6, NT>(P, blk, shared, col0, nst, ring); break;
+                                                   unsigned char* lds) {
+  if constexpr (MODE == 0) {
+    lds_gemm_na<MODE, NT, TileA>(P, blk, shared, col0, nst, lds);
+  } else if (!P.wide) {
+    lds_gemm_na<MODE, NT, TileA>(P, blk, shared, col0, nst, lds);
+  } else if (blk.n_rows <= TileW::kRows) {
+    lds_gemm_na<MODE, NT, TileW>(P, blk, shared, col0, nst, lds);
+  } else {
+    lds_gemm_na<MODE, NT, TileA>(P, blk, shared, col0, nst, lds);
+    __syncthreads();   // every wave is done with the first pass's staging area
+    lds_gemm_na<MODE, NT, TileA>(P, blk, shared, col0 + 256, nst, lds);
   }
 }
 
 template <int MODE>
 __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmParams P) {
   // the token ring during the K loop, then the output tile of the epilogue
-  constexpr int kStg = kRows * (((MODE == 0) ? 16 : 32) * kFR * kWaves * 2 + 16);
-  constexpr int kLds = kStg > kTSlots * kStage ? kStg : kTSlots * kStage;
+  // (down: the larger of the two item shapes)
+  constexpr int kStgA = TileA::kRows * (((MODE == 0) ? 16 : 32) * kWaves * 2 + 16);
+  constexpr int kStgW = MODE == 1 ? TileW::kRows * (2 * 32 * kWaves * 2 + 16) : 0;
+  constexpr int kStg = kStgA > kStgW ? kStgA : kStgW;
+  constexpr int kLds = kStg > kTSlots * TileA::kStage ? kStg : kTSlots * TileA::kStage;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[kLds];
-  auto ring = reinterpret_cast<unsigned char (*)[kStage]>(lds);
 
   // XCD-aware deal of work items.  Block b runs on XCD b % 8.  The routed
   // experts' row blocks (a prefix of the list, ordered by group) are cut into
@@ -529,7 +588,7 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
       const bool shared = blk.group == P.E;
       const int inter = shared ? P.Is : P.I;
       const int nout = (MODE == 0) ? inter : P.H;
-      const int col0 = tile * (MODE == 0 ? 128 : 256);  // first output column
+      const int col0 = tile * (MODE == 0 ? 128 : P.wide ? 512 : 256);  // first output column
       const int nst = ((MODE == 0) ? P.H : inter) >> 6;  // 64-wide k stages
       // A row block that is its group's only one is the single reader of its
       // weight tile, which then streams with non-temporal loads (a higher
@@ -537,9 +596,9 @@ __global__ __launch_bounds__(64 * kWaves) void expert_gemm_lds_kernel(LdsGemmPar
       // loads, so the blocks after the first find them in L2.
       if (col0 < nout) {                                 // uniform over the workgroup
         if (blk.n_group == 1)
-          lds_gemm_fragments<MODE, true>(P, blk, shared, col0, nst, ring);
+          lds_gemm_fragments<MODE, true>(P, blk, shared, col0, nst, lds);
         else
-          lds_gemm_fragments<MODE, false>(P, blk, shared, col0, nst, ring);
+          lds_gemm_fragments<MODE, false>(P, blk, shared, col0, nst, lds);
       }
     }
   }
@@ -571,7 +630,8 @@ hipError_t launch_gate_up_lds(const Plan& p, const GateUpArgs& a, hipStream_t s)
 }
 
 hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
-  if (p.bn != kRows || p.rb_gran != kGran || p.H % 256 || p.I % 128 || p.Is % 128)
+  if (p.bn != kRows || p.rb_gran != kGran || p.I % 128 || p.Is % 128 ||
+      (p.dn_rows_wg != 256 && p.dn_rows_wg != 512) || p.H % p.dn_rows_wg)
     return hipErrorInvalidValue;
   LdsGemmParams gp{};
   gp.wa0 = a.wd; gp.sa0 = a.sd; gp.bsrc = a.h; gp.row_w = a.row_w;
@@ -579,6 +639,7 @@ hipError_t launch_down_lds(const Plan& p, const DownArgs& a, hipStream_t s) {
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = p.Is; gp.KT = p.KT; gp.tiles = p.dn_tiles;
   gp.nrb_shared = p.Is > 0 ? (p.T + p.bn - 1) / p.bn : 0;
   gp.pool = const_cast<int32_t*>(a.n_rb) + 2;
+  gp.wide = p.dn_rows_wg == 512;
   hipLaunchKernelGGL(expert_gemm_lds_kernel<1>, dim3(lds_grid(p, p.dn_tiles, pool_pct<1>())), dim3(64 * kWaves), 0, s,
                      gp);
   return hipGetLastError();

@@ -95,6 +95,9 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     "max_H_lds": (119, 400, 16384, 8, 2, 128, 128),
     "max_I_lds": (120, 400, 256, 8, 2, 16384, 128),
     "max_I_Is_decode": (122, 12, 256, 8, 2, 16384, 16384),
+    # H % 512 == 0: 512-row down items, one 512-row pass for blocks of at
+    # most 128 rows and two 256-row passes above (shared expert: 175 rows)
+    "lds_wide_down": (130, 700, 512, 8, 2, 128, 128),
 }
 
 
@@ -571,7 +574,8 @@ def test_expert_stats_flash_decode():
 
 
 # ---------------------------------------------------------------- per-kernel intermediates
-@pytest.mark.parametrize("name", ["ragged_nb1_ksplit2", "nb2", "lds_block", "lds_I_ne_Is"])
+@pytest.mark.parametrize("name", ["ragged_nb1_ksplit2", "nb2", "lds_block", "lds_I_ne_Is",
+                                  "lds_wide_down"])
 def test_gate_up_and_down_intermediates(name):
     """The two grouped GEMMs on their own: h (SwiGLU output, expert-contiguous
     rows, then the shared rows) and o (each row already times its routing
