@@ -238,22 +238,25 @@ __global__ __launch_bounds__(256, 2) void route_logits_wide_kernel(
     }
   };
 
-  // stage s: weights of s+1 into registers (split into LDS slot (s+1)%2 at
-  // the end of the stage), tokens of s+2 into buffer (s+2)%3; LDS slot
-  // (s+1)%2 was last read in stage s-1, before its closing barrier
-  f32x4 wreg[3];
+  // stage s: weights of s+2 into register buffer s%2 (its stage-s weights
+  // went to LDS at the end of stage s-1), tokens of s+2 into buffer (s+2)%3;
+  // at the end of the stage the weights of s+1 (loaded one stage earlier)
+  // are split into LDS slot (s+1)%2, last read in stage s-1, before its
+  // closing barrier
+  f32x4 wreg[2][3];
   u32x4 xb[3][2][4];
-  load_w(wreg, 0);
+  load_w(wreg[0], 0);
+  load_w(wreg[1], 1);
   load_x(xb[0], 0);
   load_x(xb[1], 1);
-  store_w(wreg, 0);
+  store_w(wreg[0], 0);
   __syncthreads();
   auto stage = [&](auto jc, int st) {
     constexpr int J = decltype(jc)::value;   // st % 6
-    load_w(wreg, st + 1);
+    load_w(wreg[J % 2], st + 2);
     load_x(xb[(J + 2) % 3], st + 2);
     compute(J % 2, xb[J % 3]);
-    store_w(wreg, (J + 1) % 2);
+    store_w(wreg[(J + 1) % 2], (J + 1) % 2);
     __syncthreads();
   };
   int st = 0;
