@@ -409,13 +409,15 @@ __device__ inline void score_key(float l, float b, float* sg, float* kk) {
 // expert, each load coalesced over the wave's 64 experts, all in flight at
 // once.
 template <int C, int QN, int SW>
-__global__ __launch_bounds__(64) void route_topk_kernel(
+__global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E,
     int K, float scale, int norm, int biw, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ keys_out, float* __restrict__ scores_out) {
   constexpr int CB = QN == 1 ? C : 4;   // expert slots per load batch
-  const int lane = threadIdx.x;
-  const int t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  // one token per wave; a workgroup of several waves takes consecutive tokens
+  const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (t >= T) return;   // uniform over the wave (no barriers below)
 
   float key[C], sc[C];
   // expert slot c from its summed logit l: score, key, optional exports
@@ -761,9 +763,12 @@ template <int C, int QN, int SW>
 static void topk_launch(const Plan& p, const float* partial, const float* bias, float scale,
                         int norm, int biw, int32_t* topk_idx, float* topk_w, float* keys,
                         float* scores, hipStream_t s) {
-  hipLaunchKernelGGL((route_topk_kernel<C, QN, SW>), dim3(p.T), dim3(64), 0, s, partial,
-                     p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw, topk_idx, topk_w,
-                     keys, scores);
+  // one token per wave: one-wave workgroups for small batches, four-wave
+  // workgroups (a quarter of the workgroups to launch) from 1024 tokens on
+  const int wpg = p.T >= 1024 ? 4 : 1;
+  hipLaunchKernelGGL((route_topk_kernel<C, QN, SW>), dim3((p.T + wpg - 1) / wpg), dim3(64 * wpg),
+                     0, s, partial, p.route_splits, bias, p.T, p.E, p.K, scale, norm, biw,
+                     topk_idx, topk_w, keys, scores);
 }
 
 // the instantiation that reads the router's layout: [T][S][E] after the wide
