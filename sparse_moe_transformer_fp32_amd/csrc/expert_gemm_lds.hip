@@ -275,13 +275,23 @@ __device__ __forceinline__ void lds_gemm_item(const LdsGemmParams& P, const RowB
                            reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q))
                      : *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
   };
+  // In the K loop, non-temporal weight loads past the end of K read a line
+  // of this lane's token row instead (in bounds, in L2 since the last
+  // stage's token loads; unused): a re-read of the last weight stage, which
+  // streamed past L2, would add an HBM round trip to the end of every item.
+  // Ordinary weight loads re-read the last stage, an L2 hit.
   auto load_w1 = [&](u32x4 (&w)[kFR][kKC], int s, int q) {
-    const size_t off = (size_t)min(s, nst - 1) * 1024;
 #pragma unroll
-    for (int f = 0; f < kFR; ++f)
-      w[f][q] = NT ? __builtin_nontemporal_load(
-                         reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q))
-                   : *reinterpret_cast<const u32x4*>(wsrc[f] + off + 256 * q);
+    for (int f = 0; f < kFR; ++f) {
+      if constexpr (NT) {
+        const u32x4* src = s < nst
+            ? reinterpret_cast<const u32x4*>(wsrc[f] + (size_t)s * 1024 + 256 * q)
+            : reinterpret_cast<const u32x4*>(tsrc[0] + (nst - 1) * 64);
+        w[f][q] = __builtin_nontemporal_load(src);
+      } else {
+        w[f][q] = *reinterpret_cast<const u32x4*>(wsrc[f] + (size_t)min(s, nst - 1) * 1024 + 256 * q);
+      }
+    }
   };
   auto load_t1 = [&](u32x4 (&v)[kTL], int s, int i) {
     const int off = min(s, nst - 1) * 64;
