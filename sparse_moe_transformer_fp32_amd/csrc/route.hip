@@ -396,14 +396,15 @@ __device__ inline void score_key(float l, float b, float* sg, float* kk) {
   *kk = k == k ? k : -INFINITY;
 }
 
-// One 64-thread workgroup (one wave) per token: add the S split-H partial
-// logits of each expert (contiguous, loaded as 16-byte vectors, all loads
-// issued before the adds; fixed order), then sigmoid, bias and wave_select.
-// C = ceil(E/64) expert slots per lane, fixed at compile time.  QN = 16-byte
-// vectors per expert: 8 holds up to 32 splits, four experts' splits in
-// flight at a time (a 128-VGPR buffer); 1 holds up to 4 splits, every
-// expert's in flight at once, in few enough registers for a higher
-// occupancy.  Both read the [T][E][S] partial sums of route_logits_kernel.
+// One wave per token (one-wave workgroups, four waves per workgroup from
+// 1024 tokens on): add the S split-H partial logits of each expert
+// (contiguous, loaded as 16-byte vectors, all loads issued before the adds;
+// fixed order), then sigmoid, bias and wave_select.  C = ceil(E/64) expert
+// slots per lane, fixed at compile time.  QN = 16-byte vectors per expert: 8
+// holds up to 32 splits, the splits of up to five expert slots in flight at
+// a time (a 160-VGPR buffer: one round of loads for E <= 320); 1 holds up to
+// 4 splits, every expert's in flight at once, in few enough registers for a
+// higher occupancy.  Both read the [T][E][S] partial sums of route_logits_kernel.
 // QN = 0 reads the [T][S][E] partial sums of route_logits_wide_kernel, SW
 // = S splits (1, 2, 4 or 8, fixed at compile time): one float per split and
 // expert, each load coalesced over the wave's 64 experts, all in flight at
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ partial, int S, const float* __restrict__ bias, int T, int E,
     int K, float scale, int norm, int biw, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ keys_out, float* __restrict__ scores_out) {
-  constexpr int CB = QN == 1 ? C : 4;   // expert slots per load batch
+  constexpr int CB = QN == 1 ? C : (C <= 5 ? C : 4);   // expert slots per load batch
   const int lane = threadIdx.x & 63;
   // one token per wave; a workgroup of several waves takes consecutive tokens
   const int t = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
