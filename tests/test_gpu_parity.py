@@ -98,6 +98,9 @@ SMALL = {  # name: (seed, T, H, E, K, I, Is)
     # H % 512 == 0: 512-row down items, one 512-row pass for blocks of at
     # most 128 rows and two 256-row passes above (shared expert: 175 rows)
     "lds_wide_down": (130, 700, 512, 8, 2, 128, 128),
+    # T >= 1024 with T % 4 != 0: the top-K kernel's four-token workgroups end
+    # in a part-filled one (three tokens)
+    "topk_ragged_T1027": (131, 1027, 512, 20, 4, 64, 64),
 }
 
 
