@@ -839,11 +839,13 @@ def main():
     if args.workload == "decode":
         del res
         torch.cuda.empty_cache()
-        side_steps = max(5, args.steps // 5)
+        # a prefill step takes ~2 ms: 25 steps after 5 warm-up steps keep
+        # the figure steady at a fraction of a second of GPU time
+        side_steps = max(10, args.steps // 2)
         if not args.no_prefill:
             # the metric's MFMA figure is quoted at T=4096; the oracle is
             # timed on the whole batch in the same run
-            line["prefill"] = side_layer_obj("prefill", side_steps, 3,
+            line["prefill"] = side_layer_obj("prefill", side_steps, 5,
                                              cpu=not args.no_cpu_baseline)
             torch.cuda.empty_cache()
         if not args.no_dense:
@@ -856,7 +858,7 @@ def main():
             line["long"] = side_layer_obj("long", 3, 1)
             torch.cuda.empty_cache()
         if not args.no_skew:
-            line["skew"] = side_layer_obj("skew", side_steps, 3)
+            line["skew"] = side_layer_obj("skew", side_steps, 5)
             torch.cuda.empty_cache()
         if not args.no_mfma_ceiling:
             # the sustained matrix-core rate, next to the nominal 2.5 PF the
