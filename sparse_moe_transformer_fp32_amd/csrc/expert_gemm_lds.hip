@@ -127,10 +127,11 @@ typedef TileShape<2, 128, 2> TileW;
 // kernel ends when the slowest XCD does; workgroups past their XCD's own
 // items claim the pooled ones with one atomic each, and the XCDs that got
 // through their own items first take the most.  For gate/up 5% took 1.4-1.8%
-// off at T = 4096 to 32768; the down items are short enough that the claim's
-// latency and the lost L2 locality cost more than the balance gains.
+// off at T = 4096 to 32768.  Down items of 256 rows were short enough that
+// the claim's latency and the lost L2 locality cost more than the balance
+// gained; the 512-row items gain a little at T = 8192 and 32768.
 template <int MODE>
-constexpr int pool_pct() { return MODE == 0 ? 5 : 0; }
+constexpr int pool_pct() { return 5; }
 // claimer slots per XCD, in multiples of its own pool share (each claimer
 // that finds the pool empty costs a workgroup launch)
 constexpr int kPoolRoom = 3;
