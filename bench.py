@@ -623,7 +623,7 @@ def library_reference(reps=10):
     return out
 
 
-def side_layer_obj(wl_name, steps, warmup, cpu=False):
+def side_layer_obj(wl_name, steps, warmup, cpu=False, cpu_tokens=None):
     """One side workload of the default run (prefill, long, skew): whole-step
     throughput, per-layer MFMA and HBM figures, both grouped GEMMs against
     their MFMA roofline (HIP events on the launch stream; for the chained
@@ -674,7 +674,9 @@ def side_layer_obj(wl_name, steps, warmup, cpu=False):
                               "boosted": int(wl.n_boost),
                               "share_on_boosted": round(float(c[boost].sum() / c.sum()), 4)}
     if cpu:
-        out["cpu_baseline"] = cpu_baseline(r, max_tokens=wl.T, budget_s=15.0)
+        # the oracle on the whole batch (prefill) or on a bounded sample of
+        # its first tokens (skew, long: cpu_tokens), one layer
+        out["cpu_baseline"] = cpu_baseline(r, max_tokens=cpu_tokens or wl.T, budget_s=15.0)
     del r
     torch.cuda.empty_cache()
     return out
@@ -855,10 +857,12 @@ def main():
             torch.cuda.empty_cache()
         if not args.no_long:
             # the compute-bound regime: 4 chained layers at T=32768
-            line["long"] = side_layer_obj("long", 3, 1)
+            line["long"] = side_layer_obj("long", 3, 1, cpu=not args.no_cpu_baseline,
+                                          cpu_tokens=1024)
             torch.cuda.empty_cache()
         if not args.no_skew:
-            line["skew"] = side_layer_obj("skew", side_steps, 5)
+            line["skew"] = side_layer_obj("skew", side_steps, 5, cpu=not args.no_cpu_baseline,
+                                          cpu_tokens=2048)
             torch.cuda.empty_cache()
         if not args.no_mfma_ceiling:
             # the sustained matrix-core rate, next to the nominal 2.5 PF the
