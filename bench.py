@@ -150,13 +150,35 @@ def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
                     n_wg *= int(r.get(f"Grid_Size_{ax}") or 1) // max(1, int(r.get(f"Workgroup_Size_{ax}") or 1))
             except ValueError:
                 n_wg = "?"
-            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-            groups[(name, n_wg)].append(dur)
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            groups[(name, n_wg)].append((t0, t1))
         lines += ["", f"# per launch shape, from the kernel trace ({os.path.basename(trace_csv)})",
                   f"{'calls':>6} {'avg_us':>10} {'min_us':>10} {'max_us':>10} {'wgs':>7}  kernel"]
-        for (name, n_wg), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        seg_lines = []
+        for (name, n_wg), ts in sorted(groups.items(),
+                                       key=lambda kv: -sum(b - a for a, b in kv[1])):
+            d = [(b - a) / 1e3 for a, b in ts]
             lines.append(f"{len(d):6d} {sum(d) / len(d):10.2f} {min(d):10.2f} {max(d):10.2f} "
                          f"{n_wg!s:>7}  {name}")
+            # runs of dispatches separated by more than 1 ms without one
+            # (phases of the run, e.g. the sizes of a probe sweep)
+            ts = sorted(ts)
+            segs, cur = [], [ts[0]]
+            for a, b in ts[1:]:
+                if a - cur[-1][1] > 1_000_000:
+                    segs.append(cur)
+                    cur = []
+                cur.append((a, b))
+            segs.append(cur)
+            if len(segs) > 1:
+                for i, sg in enumerate(segs):
+                    dd = sorted((b - a) / 1e3 for a, b in sg)
+                    seg_lines.append(f"{i:4d} {len(dd):6d} {dd[len(dd) // 2]:10.2f} {dd[0]:10.2f} "
+                                     f"{dd[-1]:10.2f} {n_wg!s:>7}  {name}")
+        if seg_lines:
+            lines += ["", "# per run of dispatches (runs separated by more than 1 ms idle), in order",
+                      f"{'run':>4} {'calls':>6} {'med_us':>10} {'min_us':>10} {'max_us':>10} {'wgs':>7}  kernel"]
+            lines += seg_lines
     with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -349,11 +371,14 @@ def mfma_ceiling(iters: int = 65536, reps: int = 5):
 
 def short_read_ceiling(mibs=(88, 176, 264), reps=40):
     """HBM read rate of short non-temporal reads (moe_read_probe), the sizes
-    of the dense decode FFN's down weights, gate/up weights and whole layer:
-    the median of `reps` single reads timed with HIP events, each of a
-    different buffer of a rotation of over 1 GiB, so that no read finds its
-    data in the 256 MB last-level cache.  The floor of a kernel that streams
-    that many bytes once, launch included."""
+    of the dense decode FFN's down weights, gate/up weights and whole layer,
+    each read of a different buffer of a rotation of over 1 GiB, so that no
+    read finds its data in the 256 MB last-level cache: the median of `reps`
+    single reads timed with HIP events (the launch latency included), and
+    the mean of `reps` reads issued back to back between one pair of events
+    (as the dense FFN's two kernels run: each launch prepared while the
+    previous read runs).  The floor of a kernel that streams that many bytes
+    once."""
     import torch
     from sparse_moe_transformer_fp32_amd import binding as B
     sink = torch.zeros(16, dtype=torch.uint8, device="cuda")
@@ -371,9 +396,19 @@ def short_read_ceiling(mibs=(88, 176, 264), reps=40):
             b.record()
         torch.cuda.synchronize()
         ms = sorted(a.elapsed_time(b) for a, b in ev)[reps // 2]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(reps):
+            B.read_probe(bufs[i % len(bufs)], sink, True)
+        b.record()
+        torch.cuda.synchronize()
+        ms_b2b = a.elapsed_time(b) / reps
         out[f"{mib}MiB"] = {"us_per_read": round(ms * 1e3, 1),
                             "gbs": round(nb / (ms * 1e-3) / 1e9, 1),
-                            "frac_of_8tbs": round(nb / (ms * 1e-3) / 8e12, 3)}
+                            "frac_of_8tbs": round(nb / (ms * 1e-3) / 8e12, 3),
+                            "us_per_read_back_to_back": round(ms_b2b * 1e3, 1),
+                            "gbs_back_to_back": round(nb / (ms_b2b * 1e-3) / 1e9, 1),
+                            "frac_of_8tbs_back_to_back": round(nb / (ms_b2b * 1e-3) / 8e12, 3)}
         del bufs
         torch.cuda.empty_cache()
     return out
