@@ -287,12 +287,24 @@ __global__ __launch_bounds__(256) void dense_gate_up_kernel(GemmParams P, int T)
 // pipeline as the grouped kernel; the S partial sums meet in LDS and wave 0
 // adds them in slice order and writes y rounded once to bf16.  No o rows
 // and no combine pass.
+//
+// The B operands (16 tokens of h per 32-wide k step) go through LDS: read
+// straight into the MFMA's lane layout, each load instruction would touch
+// 16 rows of h for 64 bytes each; instead each wave brings its slice's U
+// k steps (16 rows x 32U columns) with loads that cover 4 rows x 256 bytes
+// (whole lines) into a private double buffer, and reads its B operands from
+// there.  A wave reads only what it wrote, and a wave's LDS accesses run in
+// order, so no barrier is needed.  16-byte chunk c of row r sits at chunk
+// c ^ r: the B reads of one k step (16 rows, one chunk column each) hit
+// distinct banks.
 template <int U>
 __global__ __launch_bounds__(512) void dense_down_kernel(const uint16_t* __restrict__ wd,
                                                          const uint16_t* __restrict__ h,
                                                          uint16_t* __restrict__ y, int T, int H,
                                                          int Isl) {
+  static_assert(U == 4, "one stage of B operands is 16 rows x 256 bytes");
   __shared__ f32x4 s_red[7 * 64];
+  __shared__ __attribute__((aligned(16))) u32x4 s_h[8][2][16 * 16];   // [wave][buffer][row x chunk]
   const int lane = threadIdx.x & 63;
   const int sl = threadIdx.x >> 6;                  // slice of this wave
   const int S = blockDim.x >> 6;
@@ -300,39 +312,63 @@ __global__ __launch_bounds__(512) void dense_down_kernel(const uint16_t* __restr
   const int rt = blockIdx.x;                        // 16-row tile of the output
   const int ksteps = Isl / 32;
   const uint16_t* aptr = wd + (size_t)sl * H * Isl + (size_t)rt * ksteps * 512 + lane * 8;
-  // B operand: token r of slice sl (rows past the batch repeat its last one)
-  const uint16_t* bptr = h + ((size_t)sl * T + min(r, T - 1)) * Isl + 8 * g;
+  // h rows of this slice: load i of a stage brings rows 4i .. 4i+3 (lane / 16
+  // picks the row, lane % 16 the 16-byte chunk); rows past the batch repeat
+  // its last one
+  const uint16_t* hrow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    hrow[i] = h + ((size_t)sl * T + min(4 * i + (lane >> 4), T - 1)) * Isl;
+  u32x4(*hb)[16 * 16] = s_h[sl];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   const int nstages = (ksteps + U - 1) / U;
-  u32x4 a0[U], b0[U], a1[U], b1[U];
-  auto load = [&](u32x4 (&a)[U], u32x4 (&b)[U], int stage) {
+  // past the end of K the loads re-read the last stage (in bounds; unused)
+  auto load_a = [&](u32x4 (&a)[U], int stage) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int ks = min(stage * U + u, ksteps - 1);
       a[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(aptr + (size_t)ks * 512));
-      b[u] = *reinterpret_cast<const u32x4*>(bptr + ks * 32);
     }
   };
-  auto compute = [&](const u32x4 (&a)[U], const u32x4 (&b)[U], int stage) {
+  // the stage's 16 x 256-byte block of h (its columns 128 stage .. +127);
+  // in a ragged last stage the chunks past the row's end re-read its last
+  // chunk (in bounds; their k steps are skipped)
+  auto load_h = [&](u32x4 (&v)[4], int stage) {
+    const int col = min(stage * U * 32 + 8 * (lane & 15), Isl - 8);
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-      if (stage * U + u < ksteps) acc = mfma16(a[u], b[u], acc);
+    for (int i = 0; i < 4; ++i) v[i] = *reinterpret_cast<const u32x4*>(hrow[i] + col);
   };
-  load(a0, b0, 0);
+  auto store_h = [&](int buf, const u32x4 (&v)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 4 * i + (lane >> 4), c = lane & 15;
+      hb[buf][row * 16 + (c ^ row)] = v[i];
+    }
+  };
+  auto compute = [&](const u32x4 (&a)[U], int buf, int stage) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (stage * U + u < ksteps) {
+        // B operand: token r, k = 32 u + 8 g .. +7 of the stage
+        const u32x4 b = hb[buf][r * 16 + ((4 * u + g) ^ r)];
+        acc = mfma16(a[u], b, acc);
+      }
+    }
+  };
+  u32x4 a0[U], a1[U], v[4];
+  load_h(v, 0);
+  load_a(a0, 0);
+  store_h(0, v);
   int st = 0;
-  for (; st + 2 < nstages; st += 2) {
-    load(a1, b1, st + 1);
-    compute(a0, b0, st);
-    load(a0, b0, st + 2);
-    compute(a1, b1, st + 1);
+  for (; st + 1 < nstages; ++st) {
+    u32x4 (&ac)[U] = (st & 1) ? a1 : a0;
+    u32x4 (&an)[U] = (st & 1) ? a0 : a1;
+    load_h(v, st + 1);
+    load_a(an, st + 1);
+    compute(ac, st & 1, st);
+    store_h((st + 1) & 1, v);
   }
-  if (st + 1 < nstages) {
-    load(a1, b1, st + 1);
-    compute(a0, b0, st);
-    compute(a1, b1, st + 1);
-  } else {
-    compute(a0, b0, st);
-  }
+  compute((st & 1) ? a1 : a0, st & 1, st);
   // slices 1 .. S-1 park their sums; slice 0 adds them in order
   if (sl > 0) s_red[(sl - 1) * 64 + lane] = acc;
   __syncthreads();
@@ -365,7 +401,7 @@ hipError_t launch_gate_up_dense(const Plan& p, const GateUpArgs& a, hipStream_t 
 
 hipError_t launch_dense_down(const Plan& p, const uint16_t* wd, const uint16_t* h, uint16_t* y,
                              hipStream_t s) {
-  if (p.T < 1 || p.T > 16 || p.E < 1 || p.E > 8 || p.H % 16 || p.I % 32)
+  if (p.T < 1 || p.T > 16 || p.E < 1 || p.E > 8 || p.H % 16 || p.I < 32 || p.I % 32)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(dense_down_kernel<4>, dim3(p.H / 16), dim3(64 * p.E), 0, s, wd, h, y, p.T,
                      p.H, p.I);
