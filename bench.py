@@ -161,7 +161,8 @@ def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
             lines.append(f"{len(d):6d} {sum(d) / len(d):10.2f} {min(d):10.2f} {max(d):10.2f} "
                          f"{n_wg!s:>7}  {name}")
             # runs of dispatches separated by more than 1 ms without one
-            # (phases of the run, e.g. the sizes of a probe sweep)
+            # (phases of the run, e.g. the sizes of a probe sweep), listed
+            # for kernels with at most 8 runs
             ts = sorted(ts)
             segs, cur = [], [ts[0]]
             for a, b in ts[1:]:
@@ -170,7 +171,7 @@ def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
                     cur = []
                 cur.append((a, b))
             segs.append(cur)
-            if len(segs) > 1:
+            if 1 < len(segs) <= 8:
                 for i, sg in enumerate(segs):
                     dd = sorted((b - a) / 1e3 for a, b in sg)
                     seg_lines.append(f"{i:4d} {len(dd):6d} {dd[len(dd) // 2]:10.2f} {dd[0]:10.2f} "
