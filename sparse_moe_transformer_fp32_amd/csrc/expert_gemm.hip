@@ -242,21 +242,63 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
   }
 }
 
-// The grid covers rb_max row blocks x tiles; workgroups past the list's end
-// exit.  A row block that is its group's only one is the single reader of
-// its weight tile, which then streams with non-temporal loads: they lift the
+// Share (%) of each XCD's work items that go to a common pool, per GEMM, and
+// the claimer workgroups per pooled item.  Per-workgroup timestamps at
+// decode (T = 16) showed the 8 XCDs streaming the same item count at rates
+// up to ~5% apart, so the kernel ended when the slowest XCD did; with the
+// pool the faster XCDs take more of the last items.  Measured against a
+// plain one-item-per-block grid: gate/up -2% with 4%, down -2.5% with 2%
+// (4% for down gained nothing: its items are a third as long, so each
+// claim's latency weighs more).
+template <int MODE>
+constexpr int reg_pool_pct() { return MODE == 0 ? 4 : 2; }
+constexpr int kRegPoolRoom = 2;
+
+// Work items are (row block, weight tile) pairs, row-block-major; only the
+// first n_rb * tiles exist.  XCD-aware deal: block b runs on XCD b % 8; the
+// items are cut into 8 contiguous ranges, one per XCD, and the last
+// reg_pool_pct() percent of every range form a common pool.  Block j of
+// XCD x runs item j of its range while j is below the range's own part;
+// the next kRegPoolRoom * (its pool share) blocks of the XCD each claim one
+// pooled item with an atomic on the GEMM's pool counter (n_rb[1] for
+// gate/up, n_rb[2] for down, zeroed by the dispatch), whichever range it
+// comes from; the rest of the grid exits.  Which CU runs an item does not
+// change its result.
+//
+// A row block that is its group's only one is the single reader of its
+// weight tile, which then streams with non-temporal loads: they lift the
 // HBM read rate (a plain read kernel moves ~6.2 TB/s with ordinary loads and
 // ~7.0 TB/s with non-temporal ones).  Tiles that several row blocks read use
 // ordinary loads, so the blocks after the first find them in L2.
 template <int MODE, int NB, int FR, int KSPLIT, int U>
 __global__ __launch_bounds__(256) void expert_gemm_kernel(GemmParams P) {
   __shared__ f32x4 s_red[red_slots<KSPLIT, FR, NB>()];
-  const int tile = blockIdx.x % P.tiles;
-  const int rbi = blockIdx.x / P.tiles;
-  // both loads at once: rbi < rb_max, so the entry is in bounds even past
-  // the list's end (where it is not used)
+  __shared__ int s_claim;
+  constexpr int kPct = reg_pool_pct<MODE>();
+  const long long n_items = (long long)*P.n_rb * P.tiles;
+  auto lo = [&](int y) { return (int)((y * n_items) >> 3); };   // first item of XCD y's range
+  auto pooled = [&](int y) { return ((lo(y + 1) - lo(y)) * kPct) / 100; };
+  auto own = [&](int y) { return lo(y + 1) - lo(y) - pooled(y); };
+  const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+  int item;
+  if (j < own(x)) {
+    item = lo(x) + j;
+  } else if (j - own(x) < kRegPoolRoom * pooled(x)) {   // uniform over the workgroup
+    int n_pool = 0;
+    for (int y = 0; y < 8; ++y) n_pool += pooled(y);
+    if (threadIdx.x == 0) s_claim = atomicAdd(const_cast<int32_t*>(P.n_rb) + 1 + MODE, 1);
+    __syncthreads();
+    int idx = s_claim;
+    if (idx >= n_pool) return;   // uniform over the workgroup
+    int y = 0;
+    while (idx >= pooled(y)) idx -= pooled(y++);
+    item = lo(y) + own(y) + idx;
+  } else {
+    return;
+  }
+  const int tile = item % P.tiles;
+  const int rbi = item / P.tiles;
   const RowBlock blk = P.rb[rbi];
-  if (rbi >= *P.n_rb) return;
   if (blk.n_group == 1)
     gemm_tile<MODE, NB, FR, KSPLIT, U, true>(P, blk, tile, s_red);
   else
@@ -414,10 +456,18 @@ hipError_t launch_dense_down(const Plan& p, const uint16_t* wd, const uint16_t* 
 // 16 x 2 x H weights and there are many small workgroups to balance.  Row
 // blocks of 32 or 64 tokens: waves own different weight rows.  Larger row
 // blocks use the LDS-pipelined kernels (expert_gemm_lds.hip).
+// grid: 8 XCDs x (the most items one XCD's range can hold, an eighth of the
+// row-block bound times the tiles, rounded up, plus its claimers)
+template <int MODE>
+static unsigned reg_grid(const Plan& p, int tiles) {
+  const long long per_xcd = ((long long)p.rb_max * tiles + 7) / 8;
+  return (unsigned)(8 * (per_xcd + kRegPoolRoom * (per_xcd * reg_pool_pct<MODE>() / 100 + 1)));
+}
+
 template <int MODE>
 static hipError_t launch_mode(const Plan& p, const GemmParams& gp, int ksplit, hipStream_t s) {
-  const int grid = p.rb_max * gp.tiles;
-  if (grid == 0) return hipSuccess;
+  if (p.rb_max == 0 || gp.tiles == 0) return hipSuccess;
+  const unsigned grid = reg_grid<MODE>(p, gp.tiles);
   switch (p.nb) {
     case 1:
       if (ksplit == 4)
