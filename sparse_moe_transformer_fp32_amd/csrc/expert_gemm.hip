@@ -59,17 +59,28 @@ __device__ inline f32x4 mfma16(const u32x4& a, const u32x4& b, const f32x4& c) {
 template <int KSPLIT, int FR, int NB>
 constexpr int red_slots() { return ((KSPLIT > 1) ? (4 - 4 / KSPLIT) : 1) * FR * NB * 64; }
 
+struct NoFill {
+  __device__ void operator()() const {}
+};
+
 // One workgroup's tile of one row block.  MODE 0: gate/up + SwiGLU.  MODE 1:
 // down + combine weight.  NT: the weight loads are non-temporal.  DENSE: the
 // row block is a whole slice of the dense FFN, whose row i is token i.
-template <int MODE, int NB, int FR, int KSPLIT, int U, bool NT, bool DENSE = false>
+// BL: the B operands (16 token rows) are read from LDS (`xl`, rows `xpitch`
+// bytes apart, row r holding token min(r, T-1)), which `fill` writes and
+// publishes right after the first weight loads are issued; the tile is then
+// run by waves 4 j .. 4 j + 3 of the workgroup, whichever j.
+template <int MODE, int NB, int FR, int KSPLIT, int U, bool NT, bool DENSE = false,
+          bool BL = false, typename Fill = NoFill>
 __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& blk, int tile,
-                                          f32x4* s_red) {
+                                          f32x4* s_red, const unsigned char* xl = nullptr,
+                                          int xpitch = 0, Fill fill = Fill{}) {
+  static_assert(!BL || (KSPLIT == 4 && NB == 1 && MODE == 0), "LDS B operands: gate/up, 4-way K split");
   constexpr int RG = 4 / KSPLIT;                       // row groups per workgroup
   constexpr int WROWS = (MODE == 0) ? 8 * FR : 16 * FR;  // output columns per wave
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = BL ? ((threadIdx.x >> 6) & 3) : (threadIdx.x >> 6);
   const int rg = wave / KSPLIT, kp = wave % KSPLIT;
   const int r = lane & 15, g = lane >> 4;
   const bool shared = blk.group == P.E;
@@ -146,9 +157,11 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
         const u32x4* src = reinterpret_cast<const u32x4*>(aptr[f] + (size_t)ks * (KSPLIT * 512));
         a[u][f] = NT ? __builtin_nontemporal_load(src) : *src;
       }
+      if constexpr (!BL) {
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + ks * (KSPLIT * 32));
+        for (int nb = 0; nb < NB; ++nb)
+          b[u][nb] = *reinterpret_cast<const u32x4*>(bptr[nb] + ks * (KSPLIT * 32));
+      }
     }
   };
   auto compute = [&](const u32x4 (&a)[U][FR], const u32x4 (&b)[U][NB], int stage) {
@@ -156,14 +169,24 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
     for (int u = 0; u < U; ++u) {
       if (stage * U + u < nsteps) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < NB; ++nb) {
+          u32x4 bv;
+          if constexpr (BL) {
+            // token r, k = 32 (kp + KSPLIT ks) + 8 g .. +7: 16-byte chunk 4 (kp + KSPLIT ks) + g
+            const int chunk = 4 * (kp + KSPLIT * (stage * U + u)) + g;
+            bv = *reinterpret_cast<const u32x4*>(xl + r * xpitch + chunk * 16);
+          } else {
+            bv = b[u][nb];
+          }
 #pragma unroll
-          for (int f = 0; f < FR; ++f) acc[f][nb] = mfma16(a[u][f], b[u][nb], acc[f][nb]);
+          for (int f = 0; f < FR; ++f) acc[f][nb] = mfma16(a[u][f], bv, acc[f][nb]);
+        }
       }
     }
   };
 
   load(a0, b0, 0);
+  if constexpr (BL) fill();
   int st = 0;
   for (; st + 2 < nstages; st += 2) {
     load(a1, b1, st + 1);
@@ -318,6 +341,56 @@ __global__ __launch_bounds__(256) void dense_gate_up_kernel(GemmParams P, int T)
   gemm_tile<0, 1, 2, 4, 4, true, true>(P, blk, tile, s_red);
 }
 
+// The same gate/up with x held in LDS, for H <= 4096: three 16-column output
+// pairs per workgroup (12 waves, four per pair as above) and one workgroup
+// per CU (x takes 128 KB of LDS).  Per-workgroup timestamps of the kernel
+// above (704 one-pair workgroups at the Flash shape, all resident at once)
+// showed that a CU streams weights at a fixed rate shared by the workgroups
+// it holds, which left the CUs with three pairs running long after those
+// with two, and that the B operand loads (each instruction 16 token rows x
+// 64 bytes, from L2) took part of that rate: a copy without them ran 13%
+// faster.  Here each workgroup brings x into LDS once with whole-line loads
+// (row r holds token min(r, T-1); rows 2H + 16 bytes apart, so the 16 rows
+// of one B read fall on distinct banks) and every CU streams at most three
+// pairs.  The last workgroup's spare groups repeat the last pair: the same
+// values to the same addresses.
+constexpr int kDenseXMaxH = 4096;
+constexpr int kDensePairs = 3;
+
+__global__ __launch_bounds__(64 * 4 * kDensePairs) void dense_gate_up_x_kernel(GemmParams P, int T,
+                                                                               int n_pairs) {
+  __shared__ f32x4 s_red[kDensePairs * red_slots<4, 2, 1>()];
+  __shared__ __attribute__((aligned(16))) unsigned char s_x[16 * (2 * kDenseXMaxH + 16)];
+  const int grp = threadIdx.x >> 8;   // four waves per pair
+  const int q = min((int)blockIdx.x * kDensePairs + grp, n_pairs - 1);
+  const int g = q / P.tiles, tile = q % P.tiles;
+  const RowBlock blk{g, g * T, T, g, 1, g * T, T, 0};
+  const int pitch = 2 * P.H + 16;
+  auto fill = [&]() {
+    constexpr int kMaxIt = (16 * kDenseXMaxH / 8 + 64 * 4 * kDensePairs - 1) / (64 * 4 * kDensePairs);
+    const int cpr = P.H / 8;              // 16-byte chunks per row
+    const int total = 16 * cpr;
+    u32x4 v[kMaxIt];
+#pragma unroll
+    for (int i = 0; i < kMaxIt; ++i) {
+      const int c = min((int)threadIdx.x + i * 64 * 4 * kDensePairs, total - 1);
+      const int r = c / cpr, col = c - r * cpr;
+      v[i] = *reinterpret_cast<const u32x4*>(P.bsrc + (size_t)min(r, T - 1) * P.H + col * 8);
+    }
+#pragma unroll
+    for (int i = 0; i < kMaxIt; ++i) {
+      const int c = (int)threadIdx.x + i * 64 * 4 * kDensePairs;
+      if (c < total) {
+        const int r = c / cpr, col = c - r * cpr;
+        *reinterpret_cast<u32x4*>(s_x + r * pitch + col * 16) = v[i];
+      }
+    }
+    __syncthreads();
+  };
+  gemm_tile<0, 1, 2, 4, 4, true, true, true>(P, blk, tile, s_red + grp * red_slots<4, 2, 1>(),
+                                             s_x, pitch, fill);
+}
+
 // Down projection of the dense FFN for a batch of at most 16 tokens, with
 // the sum over the S slices inside the workgroup:
 //   y[t, n] = sum_s h_s[t] . Wd_s[n]
@@ -437,7 +510,12 @@ hipError_t launch_gate_up_dense(const Plan& p, const GateUpArgs& a, hipStream_t 
   gp.E = p.E; gp.H = p.H; gp.I = p.I; gp.Is = 0; gp.KT = p.KT;
   gp.tiles = p.gu_tiles;
   gp.limit = a.limit;
-  hipLaunchKernelGGL(dense_gate_up_kernel, dim3(p.E * p.gu_tiles), dim3(256), 0, s, gp, p.T);
+  const int n_pairs = p.E * p.gu_tiles;
+  if (p.H <= kDenseXMaxH)
+    hipLaunchKernelGGL(dense_gate_up_x_kernel, dim3((n_pairs + kDensePairs - 1) / kDensePairs),
+                       dim3(64 * 4 * kDensePairs), 0, s, gp, p.T, n_pairs);
+  else
+    hipLaunchKernelGGL(dense_gate_up_kernel, dim3(n_pairs), dim3(256), 0, s, gp, p.T);
   return hipGetLastError();
 }
 
