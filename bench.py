@@ -188,7 +188,7 @@ def summarize_stats(csv_path, out_path, command, trace_csv=None, regex="smoe"):
 # the gate/up kernel each counter workload launches (decode: register-streaming;
 # prefill: LDS-pipelined)
 GATE_UP_KERNEL = {"decode": "void smoe::expert_gemm_kernel<0,",
-                  "dense_decode": "smoe::dense_gate_up_kernel",
+                  "dense_decode": "smoe::dense_gate_up_x_kernel",
                   "prefill": "void smoe::expert_gemm_lds_kernel<0>",
                   "long": "void smoe::expert_gemm_lds_kernel<0>",
                   "skew": "void smoe::expert_gemm_lds_kernel<0>"}
