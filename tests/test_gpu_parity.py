@@ -460,6 +460,8 @@ DENSE = {  # name: (seed, T, H, I, S)
     # T <= 16 and S <= 8: two-kernel path (slice sum inside the down kernel)
     "two_kernel_T13_S8": (156, 13, 512, 2048, 8),
     "two_kernel_T16_S2": (157, 16, 384, 768, 2),
+    # H above 4096: x does not fit in LDS, the one-pair-per-workgroup gate/up
+    "two_kernel_T3_H8192_S2": (159, 3, 8192, 256, 2),
     # T <= 16 with S > 8: the row list, the grouped kernels and the combine
     "small_T8_S16": (158, 8, 256, 1024, 16),
 }
