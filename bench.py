@@ -191,7 +191,8 @@ GATE_UP_KERNEL = {"decode": "void smoe::expert_gemm_kernel<0,",
                   "dense_decode": "smoe::dense_gate_up_x_kernel",
                   "prefill": "void smoe::expert_gemm_lds_kernel<0>",
                   "long": "void smoe::expert_gemm_lds_kernel<0>",
-                  "skew": "void smoe::expert_gemm_lds_kernel<0>"}
+                  "skew": "void smoe::expert_gemm_lds_kernel<0>",
+                  "skew_mild": "void smoe::expert_gemm_lds_kernel<0>"}
 
 
 def write_traffic(pmc_root, commands):
@@ -218,7 +219,7 @@ def write_traffic(pmc_root, commands):
             f"# a plain 1 GiB device copy: FETCH_SIZE read {cf:.0f} KiB -> factor {f_fetch:.4f};",
             f"# WRITE_SIZE read {cw:.0f} KiB -> factor {f_write:.4f}.", "# commands:"]
     head += [f"#   {c}" for c in commands]
-    for wl in ("decode", "prefill", "long", "skew", "dense_decode"):
+    for wl in ("decode", "prefill", "long", "skew", "skew_mild", "dense_decode"):
         if not os.path.isdir(os.path.join(pmc_root, f"{wl}_FETCH_SIZE")):
             continue
         fe, wr = per_kernel(wl, "FETCH_SIZE"), per_kernel(wl, "WRITE_SIZE")
