@@ -195,6 +195,15 @@ GATE_UP_KERNEL = {"decode": "void smoe::expert_gemm_kernel<0,",
                   "skew_mild": "void smoe::expert_gemm_lds_kernel<0>"}
 
 
+# the down kernel of each counter workload
+DOWN_KERNEL = {"decode": "void smoe::expert_gemm_kernel<1,",
+               "dense_decode": "void smoe::dense_down_kernel",
+               "prefill": "void smoe::expert_gemm_lds_kernel<1>",
+               "long": "void smoe::expert_gemm_lds_kernel<1>",
+               "skew": "void smoe::expert_gemm_lds_kernel<1>",
+               "skew_mild": "void smoe::expert_gemm_lds_kernel<1>"}
+
+
 def write_traffic(pmc_root, commands):
     """From rocprofv3 --pmc runs laid out as <pmc_root>/<name>_<COUNTER>/
     run_counter_collection.csv (name = copy, and any of decode / prefill /
@@ -230,11 +239,12 @@ def write_traffic(pmc_root, commands):
             b = fe[k] * 1024 * f_fetch + wr.get(k, 0.0) * 1024 * f_write
             text.append(f"{wl:8s} fetch {fe[k] * 1024 * f_fetch / 1e9:9.4f} GB  write "
                         f"{wr.get(k, 0.0) * 1024 * f_write / 1e9:9.4f} GB  {k}")
-            if k.startswith(GATE_UP_KERNEL[wl]):   # gate/up + SwiGLU of this workload
-                out[f"gate_up:{wl}"] = {"kernel": k, "bytes_per_launch": int(b),
-                                        "fetch_kib": fe[k], "write_kib": wr.get(k, 0.0),
-                                        "fetch_factor": f_fetch, "write_factor": f_write,
-                                        "source_sha": _src_sha(KERNEL_SOURCES[wl])}
+            for role, prefix in (("gate_up", GATE_UP_KERNEL[wl]), ("down", DOWN_KERNEL[wl])):
+                if k.startswith(prefix):   # the workload's gate/up + SwiGLU, or its down
+                    out[f"{role}:{wl}"] = {"kernel": k, "bytes_per_launch": int(b),
+                                           "fetch_kib": fe[k], "write_kib": wr.get(k, 0.0),
+                                           "fetch_factor": f_fetch, "write_factor": f_write,
+                                           "source_sha": _src_sha(KERNEL_SOURCES[wl])}
         with open(os.path.join(ROOT, "profiles", f"hbm_bytes_gate_up_down_{wl}.txt"), "w") as f:
             f.write("\n".join(text) + "\n")
         print("\n".join(text))
@@ -699,7 +709,7 @@ def side_layer_obj(wl_name, steps, warmup, cpu=False, cpu_tokens=None):
         "roofline_gate_up": roofline_obj("mfma", w["gu_flops"] / (gu_ms * 1e-3) / 1e12,
                                          MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", _traffic(tkey)),
         "roofline_down": roofline_obj("mfma", dn_flops / (dn_ms * 1e-3) / 1e12,
-                                      MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", None),
+                                      MFMA_BF16_PEAK_TFLOPS, "TFLOP/s", _traffic(f"down:{wl.name}")),
         "gate_up_hbm_gbs": round(w["gu_bytes"] / (gu_ms * 1e-3) / 1e9, 1),
         "stage_ms": {k: round(v, 4) for k, v in st.items()},
     }
