@@ -270,9 +270,9 @@ __device__ __forceinline__ void gemm_tile(const GemmParams& P, const RowBlock& b
 // decode (T = 16) showed the 8 XCDs streaming the same item count at rates
 // up to ~5% apart, so the kernel ended when the slowest XCD did; with the
 // pool the faster XCDs take more of the last items.  Measured against a
-// plain one-item-per-block grid: gate/up -2% with 4%, down -2.5% with 2%
-// (4% for down gained nothing: its items are a third as long, so each
-// claim's latency weighs more).
+// plain one-item-per-block grid on one box: gate/up -1.2% with 4%, down
+// -0.9% with 2% (4% for down gained nothing: its items are a third as
+// long, so each claim's latency weighs more).
 template <int MODE>
 constexpr int reg_pool_pct() { return MODE == 0 ? 4 : 2; }
 constexpr int kRegPoolRoom = 2;
