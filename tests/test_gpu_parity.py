@@ -245,6 +245,15 @@ def test_flash_decode_full():
     assert rg["counts"].sum() == 16 * 8
 
 
+def test_flash_decode_bitwise_deterministic_and_permutation_equivariant():
+    """The headline decode batch (T = 16, register kernels with their pooled
+    tail: which workgroup claims a pooled item varies from run to run), run
+    twice (bitwise equal) and once on permuted tokens."""
+    g, inp = _flash("decode")
+    print("flash case decode: run twice + permuted", flush=True)
+    _bitwise_twice_and_permuted(g, inp.wl.K, seed=5)
+
+
 def test_flash_prefill_full():
     """T = 4096 at the Flash shape (the LDS-pipelined kernels, every expert
     touched, ~114 rows each): routing on every token and the output on all
